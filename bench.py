@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache attention path on one MI355X.
+
+A step is one decode step of a 28-layer Qwen3-0.6B-shaped model at
+concurrency 64: for each layer, store the 64 new tokens' K/V (kv_store) and
+run decode attention over the paged cache (paged_decode: split-K partition
+kernel + combine kernel).  Workload: 64 seqs, context U{512..1024}, block 256,
+16 q heads / 8 KV heads / head_dim 128, bf16, 28 independent layer caches
+(7 GiB), q pre-scaled.  Inputs are synthetic, drawn with fixed seeds, resident
+in HBM before timing starts.  By default the step is captured once in a HIP
+graph and replayed (the pages' decode runs with graph replay); the eager rate
+is reported next to it.
+
+The varlen prefill over a cached prefix (16 seqs, new U{64..512}, prefix 0-2
+blocks) is timed as a second leg and reported as MFMA utilisation.
+
+Prints ONE JSON line.  `value` = algorithmic bytes of the step (K/V read by
+decode for the admitted positions, q, out, block tables, kv_store traffic) /
+step time, in GB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "paged-decode KV GB/s (% HBM peak) + attn tokens/s at c=64; prefill MFMA %"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--layers", type=int, default=28)
+    return ap.parse_args()
+
+
+def decode_bytes(ctx, bs, hq, hkv, d, window=0):
+    """Algorithmic bytes of one decode call: K and V rows of every admitted
+    position, q, out, the used block-table entries and the context lengths."""
+    kv = 0
+    tbl = 0
+    for L in ctx:
+        L = int(L)
+        lo = max(0, L - window) if window else 0
+        kv += (L - lo) * hkv * d * 2 * 2
+        tbl += (math.ceil(L / bs) - lo // bs) * 4 if L > 0 else 0
+    n = len(ctx)
+    return kv + 2 * n * hq * d * 2 + tbl + 4 * n
+
+
+def store_bytes(n, hkv, d):
+    return n * hkv * d * 2 * 2 * 2 + 4 * n
+
+
+def prefill_flops(lq, lk, hq, d, window=0):
+    """4*d flops (QK^T and PV) per admitted (query, key) pair per q head."""
+    pairs = 0
+    for q_len, k_len in zip((int(v) for v in lq), (int(v) for v in lk)):
+        p = k_len - q_len
+        for i in range(q_len):
+            t = p + i
+            lo = max(0, t - window + 1) if window else 0
+            pairs += t - lo + 1
+    return int(4 * d * pairs * hq)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}); attention shards by KV head with no "
+              f"exchange, so the per-GPU figure at N=1 is the one to read.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_236_amd as pk
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    nl = args.layers
+    hq, hkv, d, bs = W.NUM_Q_HEADS, W.NUM_KV_HEADS, W.HEAD_DIM, 256
+
+    # ---- inputs, resident before timing -------------------------------------
+    layers = []
+    for l in range(nl):
+        meta = W.deep_decode_layer_meta(l)
+        t = W.to_torch(meta, dev)
+        t["k_cache"], t["v_cache"] = W.device_caches(W.DEEP_DECODE, 256, bs, dev, layer=l)
+        t["out"] = torch.empty_like(t["q"])
+        layers.append(t)
+    ctx = meta.context_lens
+    maxctx = int(ctx.max())
+    scale = meta.scale
+    ps, nparts = pk.decode_plan(64, hkv, maxctx)
+    ws_bytes = pk.decode_workspace_size(64, hq, hkv, d, maxctx)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def store(t):
+        pk.kv_store(t["key"], t["value"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+
+    def decode(t):
+        pk.paged_decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                        scale, max_context_len=maxctx, out=t["out"], workspace=ws)
+
+    def step():
+        for t in layers:
+            store(t)
+            decode(t)
+
+    def timed(fn, steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall / steps * 1e3
+
+    for _ in range(args.warmup):
+        step()
+    eager_ms, eager_wall_ms = timed(step, args.steps)
+
+    graph = None
+    if args.mode == "graph":
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        graph_ms, graph_wall_ms = timed(graph.replay, args.steps)
+        ms_per_step = max(graph_ms, graph_wall_ms)
+    else:
+        ms_per_step = max(eager_ms, eager_wall_ms)
+
+    # ---- per-kernel duration of the decode call (events on its stream) ------
+    # A spin kernel first gives the host a head start, so the events time GPU
+    # work back to back, not host launch gaps.
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in layers]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in layers]
+    for t, s, e in zip(layers, starts, ends):
+        s.record(stream)
+        decode(t)
+        e.record(stream)
+    torch.cuda.synchronize()
+    dec_us = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / len(layers) * 1e3
+    torch.cuda._sleep(50_000_000)
+    for t, s, e in zip(layers, starts, ends):
+        s.record(stream)
+        store(t)
+        e.record(stream)
+    torch.cuda.synchronize()
+    store_us = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / len(layers) * 1e3
+
+    dbytes = decode_bytes(ctx, bs, hq, hkv, d)
+    sbytes = store_bytes(64, hkv, d)
+    step_bytes = nl * (dbytes + sbytes)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_gbs = dbytes / (dec_us * 1e-6) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode step, 28 layers x (kv_store + paged_decode), c=64",
+            "num_seqs": 64, "context_lens": "U{512..1024}", "block_size": bs,
+            "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d, "layers": nl,
+            "mode": args.mode, "partition_size": ps, "partitions_per_seq": nparts,
+        },
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "attn_tokens_per_s": round(64 / (ms_per_step * 1e-3), 1),
+        "eager_ms_per_step": round(max(eager_ms, eager_wall_ms), 4),
+        "roofline": {
+            "kernel": "paged_decode call (decode_partition_kernel + decode_combine_kernel)",
+            "bound": "hbm",
+            "achieved": round(dec_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": dbytes,
+            "us_per_launch": round(dec_us, 2),
+        },
+        "kv_store": {"us_per_launch": round(store_us, 2), "bytes_per_launch": sbytes,
+                     "GB/s": round(sbytes / (store_us * 1e-6) / 1e9, 1)},
+    }
+
+    # ---- prefill leg ----------------------------------------------------------
+    if not args.no_prefill:
+        try:
+            result["prefill"] = prefill_leg(args, pk, W, dev, stream)
+        except pk.PagedKVError as e:
+            result["prefill"] = {"error": str(e)}
+
+    # ---- CPU baseline: the oracle on a bounded sample -------------------------
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(W, dbytes)
+
+    del layers
+    print(json.dumps(result), flush=True)
+
+
+def prefill_leg(args, pk, W, dev, stream):
+    import numpy as np
+    import torch
+    x = W.prefix_prefill()
+    t = W.to_torch(x, dev)
+    lq = np.diff(x.cu_seqlens_q)
+    lk = np.diff(x.cu_seqlens_k)
+    msq = int(lq.max())
+    out = torch.empty_like(t["q"])
+
+    def run():
+        pk.paged_prefill(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["cu_seqlens_q"],
+                         t["cu_seqlens_k"], x.scale, max_seqlen_q=msq, out=out)
+
+    pk.kv_store(t["key"], t["value"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    n = max(args.steps, 10)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    flops = prefill_flops(lq, lk, W.NUM_Q_HEADS, W.HEAD_DIM)
+    tflops = flops / (us * 1e-6) / 1e12
+    return {
+        "workload": "varlen causal prefill, 16 seqs, new U{64..512}, prefix 0-2 x 256",
+        "total_q": int(lq.sum()), "us_per_launch": round(us, 2), "flops_per_launch": flops,
+        "roofline": {"kernel": "paged_prefill_kernel", "bound": "mfma",
+                     "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
+
+
+def cpu_baseline(W, dbytes_per_layer):
+    """The oracle, untuned, on the host: whole layers of the same decode
+    workload (64 seqs, all 16 heads) until ~10 s of CPU time is spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limits = threadpool_limits(1)
+    except Exception:
+        limits = None
+    secs, layers_done = 0.0, 0
+    while secs < 10.0 and layers_done < 28:
+        x = W.deep_decode_layer(layers_done)
+        kc, vc = oracle.kv_store(x.k_cache, x.v_cache, x.key, x.value, x.slot_mapping)
+        t0 = time.perf_counter()
+        oracle.paged_decode(x.q, kc, vc, x.block_tables, x.context_lens, x.scale)
+        secs += time.perf_counter() - t0
+        layers_done += 1
+    if limits is not None:
+        limits.unregister() if hasattr(limits, "unregister") else None
+    gbs = dbytes_per_layer * layers_done / secs / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{layers_done} of 28 decode layers (64 seqs x 16 heads each), "
+                      f"{secs:.1f} s, float64 NumPy, 1 thread",
+            "attn_tokens_per_s_equiv": round(64 / (secs / layers_done * 28), 3),
+            "cpu": platform.processor() or platform.machine()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * pagedkv.h — C ABI of a gfx950 (MI355X) library for attention over a paged
+ * KV cache: storing new K/V into cache blocks, decode attention (one query
+ * token per sequence, split-K with a combine pass, optional sliding window)
+ * and variable-length causal prefill over a partly cached prefix.
+ *
+ * Sources.  nano-vllm-rs README, "Run Inference" (the KV-cache block size is a
+ * user knob) and "GGUF Models" (the cache is paged); lunaryes/nano-vllm
+ * diagram, "Components" and "Connections" (a KV block manager allocates cached
+ * blocks; the model runner sets an execution context that the layers read);
+ * nano-vllm-sansho README, "Key Features" (prefix caching) and "Sansho Serving
+ * Roofline Anchors" (q=1 decode; a sliding-window-256 model).  The pages do
+ * not write the attention formula; the library computes textbook scaled-dot-
+ * product softmax attention, described with each call below.
+ *
+ * Conventions for every call
+ *  - Tensors are device pointers to contiguous row-major arrays.  bf16 is the
+ *    IEEE bfloat16 bit layout; index arrays are int32.
+ *  - KV cache layout: [num_blocks, block_size, num_kv_heads, head_dim] bf16.
+ *    A slot s is row (s % block_size) of block (s / block_size).
+ *  - Logical position j of sequence b lives in slot
+ *      block_tables[b * max_blocks_per_seq + j / block_size] * block_size
+ *        + j % block_size.
+ *  - Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *  - Supported shapes: head_dim == 128; num_q_heads / num_kv_heads in
+ *    {1, 2, 4, 8}; block_size a multiple of 16 in [16, 1024].
+ *  - The caller owns every buffer.  The library allocates and frees no device
+ *    memory.  Workspace, where needed, is caller-provided after a size query.
+ *  - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *    default stream) and returns; results are visible to later work on the
+ *    same stream.  Calls are thread-safe.
+ *  - Host-side argument checks never touch device memory.  A non-OK status
+ *    means nothing was launched; pk_last_error_message() then describes the
+ *    problem (thread-local).  No C++ exception crosses this ABI.
+ *  - Indices read from device memory (slots, block-table entries) are
+ *    bounds-checked in the kernels: an out-of-range slot is not stored and an
+ *    out-of-range block-table entry contributes no keys, so a bad table can
+ *    give a wrong answer but never an out-of-bounds access.
+ *  - `out` must not alias any input; `key`/`value` must not alias the caches.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pk_status {
+  PK_OK = 0,
+  PK_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent sizes */
+  PK_ERR_UNSUPPORTED = 2,   /* a shape this build does not implement          */
+  PK_ERR_WORKSPACE = 3,     /* decode workspace missing or too small           */
+  PK_ERR_LAUNCH = 4         /* the HIP runtime rejected a kernel launch        */
+} pk_status;
+
+/* Library version string, e.g. "pagedkv 0.1.0 gfx950". */
+const char* pk_version(void);
+/* Name of a status code; never NULL. */
+const char* pk_status_string(pk_status s);
+/* Detail for the last non-OK status returned on this thread ("" if none). */
+const char* pk_last_error_message(void);
+
+/*
+ * pk_kv_store — store the K/V rows of new tokens into the paged cache.
+ * (the slot_mapping scatter: each new token's K/V go to the slot the block
+ * manager gave it; nano-vllm-rs README "GGUF Models", lunaryes/nano-vllm
+ * "Connections": the scheduler's block manager allocates cached blocks.)
+ *
+ *   key, value    bf16 [num_tokens, num_kv_heads, head_dim]
+ *   slot_mapping  int32 [num_tokens]; slot of token i, or -1 to skip token i
+ *                 (padding).  Slots >= num_blocks * block_size are skipped too.
+ *                 Valid slots must be distinct (otherwise which write lands is
+ *                 unspecified).
+ *   k_cache, v_cache  bf16 [num_blocks, block_size, num_kv_heads, head_dim]
+ *
+ * The copy is bit-exact.  num_tokens == 0 is a no-op.
+ */
+pk_status pk_kv_store(const void* key, const void* value,
+                      const int32_t* slot_mapping, int32_t num_tokens,
+                      void* k_cache, void* v_cache,
+                      int32_t num_blocks, int32_t block_size,
+                      int32_t num_kv_heads, int32_t head_dim, void* stream);
+
+/*
+ * Decode split planning.  Decode work for one (sequence, KV head) is cut into
+ * partitions of `partition_size` tokens (a multiple of 64); each partition is
+ * reduced by one workgroup to a partial softmax state, and a combine kernel
+ * merges the partials (split-K / flash-decoding).  When every sequence fits
+ * one partition the combine pass is skipped and the partition kernel writes
+ * the output directly.
+ *
+ * pk_paged_decode_plan: the partition size and the number of partition slots
+ * per sequence that pk_paged_decode will use for these arguments.
+ * `partition_size_request` 0 asks for the built-in choice; otherwise it must
+ * be a positive multiple of 64.
+ */
+pk_status pk_paged_decode_plan(int32_t num_seqs, int32_t num_kv_heads,
+                               int32_t max_context_len, int32_t sliding_window,
+                               int32_t partition_size_request,
+                               int32_t* partition_size_out,
+                               int32_t* num_partitions_out);
+
+/* Workspace bytes pk_paged_decode needs for the same arguments (0 when the
+ * plan has a single partition), or 0 with the status set if the arguments are
+ * invalid. */
+size_t pk_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t max_context_len,
+                                      int32_t sliding_window,
+                                      int32_t partition_size_request);
+
+/*
+ * pk_paged_decode — attention for one query token per sequence over the
+ * paged cache (the q=1 decode step; nano-vllm-sansho README "Sansho Serving
+ * Roofline Anchors"), with an optional sliding window (its SWA-256 model).
+ *
+ *   out           bf16 [num_seqs, num_q_heads, head_dim]
+ *   q             bf16 [num_seqs, num_q_heads, head_dim]
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]; entries past
+ *                 ceil(context_lens[b] / block_size) are never read
+ *   context_lens  int32 [num_seqs]; L_b keys, including the new token, which
+ *                 is the query (it must already be stored, e.g. by
+ *                 pk_kv_store earlier on the same stream).  Values are clamped
+ *                 to [0, max_blocks_per_seq * block_size].
+ *   max_context_len  host-side upper bound of context_lens, used to plan the
+ *                 split; keys of a sequence beyond it are not attended.
+ *   scale         softmax scale applied to q.k (1/sqrt(head_dim) usually)
+ *   sliding_window  0: attend keys 0..L-1; W > 0: keys max(0, L-W)..L-1
+ *   workspace     fp32 scratch of at least pk_paged_decode_workspace_size()
+ *                 bytes (may be NULL when that size is 0); its contents are
+ *                 dead after the call's kernels finish
+ *
+ * out[b, h] = sum_j softmax_j(scale * q[b,h] . K_j) V_j over the admitted j,
+ * computed with fp32 accumulation and rounded to bf16 (nearest even).  A
+ * sequence with L_b == 0 gets a zero row.
+ */
+pk_status pk_paged_decode(void* out, const void* q,
+                          const void* k_cache, const void* v_cache,
+                          int32_t num_blocks, int32_t block_size,
+                          int32_t num_kv_heads, int32_t head_dim,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t max_context_len,
+                          float scale, int32_t sliding_window,
+                          int32_t partition_size_request,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * pk_paged_prefill — variable-length causal attention for the new tokens of
+ * several sequences whose prefix may already be cached (prefix caching:
+ * nano-vllm-sansho README "Key Features"; prefill and decode as separate
+ * phases: lunaryes/nano-vllm introduction).
+ *
+ *   out           bf16 [total_q, num_q_heads, head_dim]
+ *   q             bf16 [total_q, num_q_heads, head_dim]; sequence b owns rows
+ *                 cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *   cu_seqlens_q  int32 [num_seqs + 1], non-decreasing, cu_seqlens_q[0] == 0,
+ *                 cu_seqlens_q[num_seqs] == total_q
+ *   cu_seqlens_k  int32 [num_seqs + 1]; Lk_b = cu_seqlens_k[b+1] -
+ *                 cu_seqlens_k[b] keys of sequence b are in the cache (prefix
+ *                 and new tokens; store the new ones first with pk_kv_store)
+ *   max_seqlen_q  host-side upper bound of the per-sequence query counts;
+ *                 queries beyond it are not computed
+ *   max_blocks_per_seq  at most 2048 (the touched table entries are staged
+ *                 on chip); larger values return PK_ERR_UNSUPPORTED
+ *   scale, sliding_window  as for decode
+ *
+ * With prefix P_b = Lk_b - Lq_b, new query i of sequence b sits at position
+ * P_b + i and attends keys j <= P_b + i (and P_b + i - j < W when W > 0).
+ * Sequences with Lk_b < Lq_b are invalid; their rows are left unwritten.
+ */
+pk_status pk_paged_prefill(void* out, const void* q,
+                           const void* k_cache, const void* v_cache,
+                           int32_t num_blocks, int32_t block_size,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                           int32_t num_q_heads, float scale, int32_t sliding_window,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,221 @@
+"""Paged KV-cache attention for MI355X (gfx950): Python binding of libpagedkv.so.
+
+Thin argument marshalling over the C ABI declared in include/pagedkv.h: torch
+tensors are checked for dtype, device and contiguity, and passed as raw device
+pointers together with torch's current HIP stream.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.  If the
+library has not been built, importing this package raises ImportError.
+
+    kv_store(key, value, slot_mapping, k_cache, v_cache)
+    paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ...)
+    paged_prefill(q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k, scale, ...)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "PagedKVError", "version", "kv_store", "paged_decode", "paged_prefill",
+    "decode_plan", "decode_workspace_size",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_236_amd.build` "
+        "(or __graft_entry__.build()); there is no non-HIP implementation")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i32 = ctypes.c_int32
+_p = ctypes.c_void_p
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_lib.pk_version.restype = ctypes.c_char_p
+_lib.pk_version.argtypes = []
+_lib.pk_status_string.restype = ctypes.c_char_p
+_lib.pk_status_string.argtypes = [ctypes.c_int]
+_lib.pk_last_error_message.restype = ctypes.c_char_p
+_lib.pk_last_error_message.argtypes = []
+_lib.pk_kv_store.restype = ctypes.c_int
+_lib.pk_kv_store.argtypes = [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _p]
+_lib.pk_paged_decode_plan.restype = ctypes.c_int
+_lib.pk_paged_decode_plan.argtypes = [_i32, _i32, _i32, _i32, _i32,
+                                      ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+_lib.pk_paged_decode_workspace_size.restype = _sz
+_lib.pk_paged_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
+_lib.pk_paged_decode.restype = ctypes.c_int
+_lib.pk_paged_decode.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p, _i32,
+                                 _i32, _i32, _f32, _i32, _i32, _p, _sz, _p]
+_lib.pk_paged_prefill.restype = ctypes.c_int
+_lib.pk_paged_prefill.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p, _p,
+                                  _i32, _i32, _i32, _i32, _f32, _i32, _p]
+
+
+class PagedKVError(RuntimeError):
+    """A non-OK status from the C ABI."""
+
+    def __init__(self, status: int, message: str):
+        self.status = status
+        name = _lib.pk_status_string(status).decode()
+        super().__init__(f"{name}: {message}")
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise PagedKVError(status, _lib.pk_last_error_message().decode())
+
+
+def version() -> str:
+    return _lib.pk_version().decode()
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, device=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must both be [num_blocks, block_size, num_kv_heads, head_dim]")
+    return tuple(int(x) for x in k_cache.shape)
+
+
+def kv_store(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
+             k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Store key/value [num_tokens, num_kv_heads, head_dim] (bf16) into the
+    caches at slot_mapping (int32 [num_tokens]; -1 skips a token)."""
+    nb, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    dev = k_cache.device
+    n = int(slot_mapping.numel())
+    if key.shape != (n, hkv, d) or value.shape != (n, hkv, d):
+        raise ValueError(f"key/value must be [{n}, {hkv}, {d}]")
+    _check(_lib.pk_kv_store(
+        _dev(key, "key", torch.bfloat16, dev), _dev(value, "value", torch.bfloat16, dev),
+        _dev(slot_mapping, "slot_mapping", torch.int32, dev), n,
+        _dev(k_cache, "k_cache", torch.bfloat16, dev), _dev(v_cache, "v_cache", torch.bfloat16, dev),
+        nb, bs, hkv, d, _stream(dev)))
+
+
+def decode_plan(num_seqs: int, num_kv_heads: int, max_context_len: int,
+                sliding_window: int = 0, partition_size: int = 0):
+    """(partition_size, partition slots per sequence) that paged_decode uses."""
+    ps, nparts = _i32(), _i32()
+    _check(_lib.pk_paged_decode_plan(num_seqs, num_kv_heads, max_context_len, sliding_window,
+                                     partition_size, ctypes.byref(ps), ctypes.byref(nparts)))
+    return ps.value, nparts.value
+
+
+def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          max_context_len: int, sliding_window: int = 0,
+                          partition_size: int = 0) -> int:
+    n = _lib.pk_paged_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                            max_context_len, sliding_window, partition_size)
+    msg = _lib.pk_last_error_message().decode()
+    if n == 0 and msg:
+        raise PagedKVError(1, msg)
+    return int(n)
+
+
+_workspaces = {}
+
+
+def _workspace(device, nbytes: int) -> Optional[torch.Tensor]:
+    """A grow-only per-device scratch buffer for the split-K partials."""
+    if nbytes == 0:
+        return None
+    key = (device.type, device.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, *,
+                 sliding_window: int = 0, max_context_len: Optional[int] = None,
+                 out: Optional[torch.Tensor] = None, partition_size: int = 0,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention: q [num_seqs, num_q_heads, 128] bf16 -> out (same shape).
+
+    max_context_len defaults to context_lens.max() (a device-to-host sync);
+    pass it to keep the call asynchronous.
+    """
+    nb, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    dev = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
+    nseq, hq, qd = (int(x) for x in q.shape)
+    if qd != d:
+        raise ValueError("q and cache head_dim differ")
+    if block_tables.dim() != 2 or block_tables.shape[0] != nseq or context_lens.shape != (nseq,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks] and context_lens [num_seqs]")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if nseq else 0
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    need = decode_workspace_size(nseq, hq, hkv, d, max_context_len, sliding_window, partition_size)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    ws_ptr = _dev(workspace, "workspace", torch.uint8, dev) if workspace is not None else None
+    ws_bytes = int(workspace.numel()) if workspace is not None else 0
+    _check(_lib.pk_paged_decode(
+        _dev(out, "out", torch.bfloat16, dev), _dev(q, "q", torch.bfloat16, dev),
+        _dev(k_cache, "k_cache", torch.bfloat16, dev), _dev(v_cache, "v_cache", torch.bfloat16, dev),
+        nb, bs, hkv, d,
+        _dev(block_tables, "block_tables", torch.int32, dev), int(block_tables.shape[1]),
+        _dev(context_lens, "context_lens", torch.int32, dev), nseq, hq, max_context_len,
+        float(scale), sliding_window, partition_size, ws_ptr, ws_bytes, _stream(dev)))
+    return out
+
+
+def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  block_tables: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                  cu_seqlens_k: torch.Tensor, scale: float, *, max_seqlen_q: int,
+                  sliding_window: int = 0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Varlen causal prefill: q [total_q, num_q_heads, 128] bf16 -> out (same shape)."""
+    nb, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    dev = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [total_q, num_q_heads, head_dim]")
+    total_q, hq, qd = (int(x) for x in q.shape)
+    if qd != d:
+        raise ValueError("q and cache head_dim differ")
+    nseq = int(cu_seqlens_q.numel()) - 1
+    if nseq < 0 or cu_seqlens_k.shape != cu_seqlens_q.shape or block_tables.dim() != 2 \
+            or block_tables.shape[0] != nseq:
+        raise ValueError("cu_seqlens_q/k must be [num_seqs+1] and block_tables [num_seqs, max_blocks]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _check(_lib.pk_paged_prefill(
+        _dev(out, "out", torch.bfloat16, dev), _dev(q, "q", torch.bfloat16, dev),
+        _dev(k_cache, "k_cache", torch.bfloat16, dev), _dev(v_cache, "v_cache", torch.bfloat16, dev),
+        nb, bs, hkv, d,
+        _dev(block_tables, "block_tables", torch.int32, dev), int(block_tables.shape[1]),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev),
+        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev),
+        nseq, total_q, int(max_seqlen_q), hq, float(scale), sliding_window, _stream(dev)))
+    return out

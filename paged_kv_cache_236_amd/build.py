@@ -1,0 +1,75 @@
+"""Build step: compile the HIP sources under csrc/ into libpagedkv.so (gfx950).
+
+Run as ``python -m paged_kv_cache_236_amd.build`` or through
+``__graft_entry__.build()``.  The library is built in-tree, next to this file.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libpagedkv.so")
+PROBE = os.path.join(HERE, "hbm_read_probe")
+ARCH = "gfx950"
+
+# Packed-fp32 VALU forms are kept out of generated code: ordinary float code is
+# compiled to scalar-lane fp32 instructions.
+HIP_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP toolchain (ROCm) is required to build libpagedkv.so")
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every HIP source into one shared library; returns its path."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, *extra_flags,
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
+           *sources(), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {r.returncode}")
+    if verbose and r.stderr.strip():
+        sys.stderr.write(r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The HBM read-ceiling / copy-calibration probe (a stand-alone program)."""
+    cmd = [hipcc(), "-O3", f"--offload-arch={ARCH}",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           os.path.join(HERE, "probe", "hbm_read_probe.hip"), "-o", PROBE]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {r.returncode}")
+    return PROBE
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
+    print(build_probe(verbose=True))

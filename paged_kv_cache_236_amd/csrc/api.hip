@@ -1,0 +1,294 @@
+// The C ABI (include/pagedkv.h): argument validation, decode split planning,
+// workspace sizing and status reporting.  Validation reads only host values,
+// never device memory, so every error path can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+#include "pagedkv.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pk_status fail(pk_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+pk_status ok() {
+  g_last_error.clear();
+  return PK_OK;
+}
+
+constexpr double kLog2e = 1.4426950408889634;
+constexpr int32_t kHeadDim = 128;
+constexpr int64_t kPartitionQuantum = 64;   // 4 wavefronts x 16-token chunks
+
+bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+pk_status check_cache_shape(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                            int32_t head_dim) {
+  if (num_blocks <= 0) return fail(PK_ERR_INVALID_ARG, "num_blocks must be > 0 (got %d)", num_blocks);
+  if (num_kv_heads <= 0) return fail(PK_ERR_INVALID_ARG, "num_kv_heads must be > 0 (got %d)", num_kv_heads);
+  if (head_dim != kHeadDim)
+    return fail(PK_ERR_UNSUPPORTED, "head_dim %d is not supported (only 128)", head_dim);
+  if (block_size < 16 || block_size > 1024 || block_size % 16 != 0)
+    return fail(PK_ERR_UNSUPPORTED,
+                "block_size %d is not supported (a multiple of 16 in [16, 1024])", block_size);
+  const int64_t elems = static_cast<int64_t>(num_blocks) * block_size * num_kv_heads * head_dim;
+  if (elems / head_dim / num_kv_heads / block_size != num_blocks)
+    return fail(PK_ERR_INVALID_ARG, "cache size overflows");
+  return PK_OK;
+}
+
+pk_status check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_q_heads <= 0) return fail(PK_ERR_INVALID_ARG, "num_q_heads must be > 0 (got %d)", num_q_heads);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PK_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (!supported_group(num_q_heads / num_kv_heads))
+    return fail(PK_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads = %d is not in {1, 2, 4, 8}",
+                num_q_heads / num_kv_heads);
+  return PK_OK;
+}
+
+struct Plan {
+  int32_t partition_size;
+  int32_t num_parts;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Partition slots a sequence can touch: ceil(L/PS) without a window; a window
+// of W keys starting anywhere inside a partition spans at most
+// (W + PS - 2) / PS + 1 partitions.
+int64_t slots_for(int64_t max_ctx, int64_t window, int64_t ps) {
+  int64_t n = ceil_div(max_ctx, ps);
+  if (window > 0) n = std::min(n, (window + ps - 2) / ps + 1);
+  return std::max<int64_t>(n, 1);
+}
+
+pk_status plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                      int32_t sliding_window, int32_t request, Plan* plan) {
+  if (num_seqs < 0) return fail(PK_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (num_kv_heads <= 0) return fail(PK_ERR_INVALID_ARG, "num_kv_heads must be > 0 (got %d)", num_kv_heads);
+  if (max_context_len < 0)
+    return fail(PK_ERR_INVALID_ARG, "max_context_len must be >= 0 (got %d)", max_context_len);
+  if (sliding_window < 0)
+    return fail(PK_ERR_INVALID_ARG, "sliding_window must be >= 0 (got %d)", sliding_window);
+  if (request < 0 || request % kPartitionQuantum != 0)
+    return fail(PK_ERR_INVALID_ARG, "partition_size_request %d must be 0 or a positive multiple of 64",
+                request);
+  const int64_t ctx = std::max<int32_t>(max_context_len, 1);
+  int64_t ps = request;
+  if (ps == 0) {
+    // Largest partition (<= 1024 tokens) that still gives >= 2048 workgroups,
+    // i.e. >= 8 per compute unit, so the 256 CUs stay busy through the tail.
+    const int64_t pairs = static_cast<int64_t>(std::max(num_seqs, 1)) * num_kv_heads;
+    ps = 1024;
+    while (ps > kPartitionQuantum && pairs * slots_for(ctx, sliding_window, ps) < 2048) ps /= 2;
+  }
+  const int64_t slots = slots_for(ctx, sliding_window, ps);
+  if (slots > 65535) return fail(PK_ERR_UNSUPPORTED, "too many partitions (%lld)", (long long)slots);
+  plan->partition_size = static_cast<int32_t>(ps);
+  plan->num_parts = static_cast<int32_t>(slots);
+  return PK_OK;
+}
+
+size_t workspace_bytes_for(int32_t num_seqs, int32_t num_q_heads, const Plan& p) {
+  if (p.num_parts <= 1) return 0;
+  const size_t heads = static_cast<size_t>(num_seqs) * num_q_heads * p.num_parts;
+  const size_t acc = heads * kHeadDim * sizeof(float);
+  const size_t acc_aligned = (acc + 255) / 256 * 256;
+  return acc_aligned + heads * 2 * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pk_version(void) { return "pagedkv 0.1.0 gfx950"; }
+
+const char* pk_status_string(pk_status s) {
+  switch (s) {
+    case PK_OK: return "PK_OK";
+    case PK_ERR_INVALID_ARG: return "PK_ERR_INVALID_ARG";
+    case PK_ERR_UNSUPPORTED: return "PK_ERR_UNSUPPORTED";
+    case PK_ERR_WORKSPACE: return "PK_ERR_WORKSPACE";
+    case PK_ERR_LAUNCH: return "PK_ERR_LAUNCH";
+  }
+  return "PK_ERR_UNKNOWN";
+}
+
+const char* pk_last_error_message(void) { return g_last_error.c_str(); }
+
+pk_status pk_kv_store(const void* key, const void* value, const int32_t* slot_mapping,
+                      int32_t num_tokens, void* k_cache, void* v_cache, int32_t num_blocks,
+                      int32_t block_size, int32_t num_kv_heads, int32_t head_dim, void* stream) {
+  if (num_tokens < 0) return fail(PK_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %d)", num_tokens);
+  if (num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PK_ERR_INVALID_ARG, "cache dimensions must be > 0");
+  if ((static_cast<int64_t>(num_kv_heads) * head_dim) % 8 != 0)
+    return fail(PK_ERR_UNSUPPORTED, "num_kv_heads * head_dim must be a multiple of 8");
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !slot_mapping || !k_cache || !v_cache)
+    return fail(PK_ERR_INVALID_ARG, "null pointer argument");
+  pk::StoreArgs a;
+  a.key = key;
+  a.value = value;
+  a.slot_mapping = slot_mapping;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_tokens = num_tokens;
+  a.row_vecs = static_cast<int32_t>(static_cast<int64_t>(num_kv_heads) * head_dim / 8);
+  a.num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  const hipError_t e = pk::launch_kv_store(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PK_ERR_LAUNCH, "kv_store launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+pk_status pk_paged_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                               int32_t sliding_window, int32_t partition_size_request,
+                               int32_t* partition_size_out, int32_t* num_partitions_out) {
+  Plan p;
+  const pk_status s = plan_decode(num_seqs, num_kv_heads, max_context_len, sliding_window,
+                                  partition_size_request, &p);
+  if (s != PK_OK) return s;
+  if (partition_size_out) *partition_size_out = p.partition_size;
+  if (num_partitions_out) *num_partitions_out = p.num_parts;
+  return ok();
+}
+
+size_t pk_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t max_context_len,
+                                      int32_t sliding_window, int32_t partition_size_request) {
+  if (head_dim != kHeadDim) {
+    fail(PK_ERR_UNSUPPORTED, "head_dim %d is not supported (only 128)", head_dim);
+    return 0;
+  }
+  if (num_kv_heads <= 0 || check_heads(num_q_heads, num_kv_heads) != PK_OK) {
+    if (num_kv_heads <= 0) fail(PK_ERR_INVALID_ARG, "num_kv_heads must be > 0");
+    return 0;
+  }
+  Plan p;
+  if (plan_decode(num_seqs, num_kv_heads, max_context_len, sliding_window, partition_size_request,
+                  &p) != PK_OK)
+    return 0;
+  ok();
+  return workspace_bytes_for(num_seqs, num_q_heads, p);
+}
+
+pk_status pk_paged_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                          int32_t head_dim, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                          float scale, int32_t sliding_window, int32_t partition_size_request,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  pk_status s = check_cache_shape(num_blocks, block_size, num_kv_heads, head_dim);
+  if (s != PK_OK) return s;
+  if ((s = check_heads(num_q_heads, num_kv_heads)) != PK_OK) return s;
+  if (max_blocks_per_seq <= 0)
+    return fail(PK_ERR_INVALID_ARG, "max_blocks_per_seq must be > 0 (got %d)", max_blocks_per_seq);
+  if (!std::isfinite(scale)) return fail(PK_ERR_INVALID_ARG, "scale must be finite");
+  Plan p;
+  if ((s = plan_decode(num_seqs, num_kv_heads, max_context_len, sliding_window,
+                       partition_size_request, &p)) != PK_OK)
+    return s;
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PK_ERR_INVALID_ARG, "null pointer argument");
+  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, p);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PK_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(PK_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  pk::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  const size_t heads = static_cast<size_t>(num_seqs) * num_q_heads * p.num_parts;
+  a.ws_acc = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                            (heads * kHeadDim * sizeof(float) + 255) / 256 * 256)
+                 : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.sliding_window = sliding_window;
+  a.partition_size = p.partition_size;
+  a.num_parts = p.num_parts;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
+  const hipError_t e = pk::launch_paged_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PK_ERR_LAUNCH, "paged_decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+pk_status pk_paged_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                           int32_t head_dim, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t total_q,
+                           int32_t max_seqlen_q, int32_t num_q_heads, float scale,
+                           int32_t sliding_window, void* stream) {
+  pk_status s = check_cache_shape(num_blocks, block_size, num_kv_heads, head_dim);
+  if (s != PK_OK) return s;
+  if ((s = check_heads(num_q_heads, num_kv_heads)) != PK_OK) return s;
+  if (max_blocks_per_seq <= 0)
+    return fail(PK_ERR_INVALID_ARG, "max_blocks_per_seq must be > 0 (got %d)", max_blocks_per_seq);
+  if (max_blocks_per_seq > pk::kPrefillMaxBlocksPerSeq)
+    return fail(PK_ERR_UNSUPPORTED, "paged_prefill supports max_blocks_per_seq <= %d (got %d)",
+                pk::kPrefillMaxBlocksPerSeq, max_blocks_per_seq);
+  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0)
+    return fail(PK_ERR_INVALID_ARG, "num_seqs, total_q and max_seqlen_q must be >= 0");
+  if (sliding_window < 0)
+    return fail(PK_ERR_INVALID_ARG, "sliding_window must be >= 0 (got %d)", sliding_window);
+  if (!std::isfinite(scale)) return fail(PK_ERR_INVALID_ARG, "scale must be finite");
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(PK_ERR_INVALID_ARG, "null pointer argument");
+  pk::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.max_seqlen_q = max_seqlen_q;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.sliding_window = sliding_window;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
+  const hipError_t e = pk::launch_paged_prefill(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported)
+    return fail(PK_ERR_UNSUPPORTED, "paged_prefill: this configuration is not implemented");
+  if (e != hipSuccess) return fail(PK_ERR_LAUNCH, "paged_prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

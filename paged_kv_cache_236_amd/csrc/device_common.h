@@ -1,0 +1,59 @@
+// Device helpers shared by the gfx950 kernels of the paged-KV library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pk {
+
+constexpr int kHeadDim = 128;   // the only head size the kernels implement
+constexpr int kWave = 64;       // CDNA wavefront width
+
+// A bf16 value is the upper 16 bits of a float32: widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float32 -> bf16 bits, round to nearest even.  NaN inputs keep a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Unpack 8 bf16 (one 128-bit load) to float32.
+__device__ __forceinline__ void unpack8(const uint4& w, float* f) {
+  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
+  f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
+  f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+
+// DPP lane moves within a row of 16 lanes (row_mask/bank_mask all enabled).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i within 8 lanes
+constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i within 16 lanes
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<kDppQuadXor1>(x);
+  x += dpp_mov<kDppQuadXor2>(x);
+  x += dpp_mov<kDppRowHalfMirror>(x);
+  x += dpp_mov<kDppRowMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, kWave); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pk

@@ -1,0 +1,70 @@
+// Host-side launchers of the kernels; called by the C ABI layer (api.hip)
+// after it has validated every argument.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pk {
+
+// Longest block-table row paged_prefill accepts (its entries are staged in LDS).
+constexpr int kPrefillMaxBlocksPerSeq = 2048;
+
+struct StoreArgs {
+  const void* key;
+  const void* value;
+  const int32_t* slot_mapping;
+  void* k_cache;
+  void* v_cache;
+  int32_t num_tokens;
+  int32_t row_vecs;        // 16-byte vectors per token row (num_kv_heads * head_dim / 8)
+  int64_t num_slots;       // num_blocks * block_size
+};
+hipError_t launch_kv_store(const StoreArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_acc;           // [num_seqs, num_q_heads, num_parts, 128] fp32 (split only)
+  float* ws_ml;            // [num_seqs, num_q_heads, num_parts, 2] fp32 (split only)
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t group;           // q heads per kv head
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int32_t max_context_len;
+  int32_t sliding_window;
+  int32_t partition_size;
+  int32_t num_parts;       // partition slots per sequence
+  float scale_log2;        // softmax scale * log2(e)
+};
+hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int32_t num_seqs;
+  int32_t total_q;
+  int32_t max_seqlen_q;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int32_t sliding_window;
+  float scale_log2;
+};
+hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pk

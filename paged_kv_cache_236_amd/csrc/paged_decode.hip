@@ -1,0 +1,367 @@
+// paged_decode: attention of one query token per sequence over the paged KV
+// cache (nano-vllm-sansho README, "Sansho Serving Roofline Anchors": the q=1
+// decode step, and its sliding-window-256 model), split over the context
+// (flash-decoding) with a separate combine kernel.
+//
+// Work decomposition.  For (sequence b, KV head g) the admitted key positions
+// [lo, L) are cut into partitions of PS tokens aligned at multiples of PS.
+// One workgroup of NW wavefronts reduces one partition; it serves all G query
+// heads that share KV head g, so every K/V byte is read from HBM exactly once.
+//
+// Inside a wavefront each lane owns 16 bytes (8 dims) of a 256-byte head row,
+// so one 128-bit load per lane covers 4 consecutive tokens (rows of 16 lanes).
+// Tokens are taken in chunks of 16 (four such loads for K and four for V);
+// a chunk never straddles a cache block because block_size is a multiple of 16,
+// so one block-table entry serves the whole chunk.  Each 16-lane row keeps its
+// own online-softmax state (running max m, sum l, fp32 accumulator), so the
+// inner loop needs no cross-row traffic: q.k is reduced over the row's 16 lanes
+// with DPP moves, everything else is lane-local.  Rows, then wavefronts, are
+// merged only once at the end (shuffles, then LDS).  The next chunk's loads
+// are issued before the current chunk is consumed, so each wavefront keeps two
+// chunks (16 KiB) of loads in flight.
+//
+// Scores are kept in the log2 domain: q is pre-multiplied by scale*log2(e) in
+// fp32 and the hardware exp2 is used.
+//
+// A partition's result is either written as the final bf16 output (when the
+// sequence has a single partition) or as the partial state (m, l, acc) that
+// the combine kernel merges: out = sum_p 2^(m_p-M) acc_p / sum_p 2^(m_p-M) l_p.
+#include "device_common.h"
+#include "launch.h"
+
+// Tuning knobs (compile-time): wavefronts per workgroup, 128-bit loads per
+// chunk for K (and as many for V; a chunk is 4 tokens per load), and whether
+// K/V loads carry the non-temporal hint (the cache is streamed once).
+#ifndef PK_DECODE_WAVES
+#define PK_DECODE_WAVES 4
+#endif
+#ifndef PK_DECODE_LOADS
+#define PK_DECODE_LOADS 4
+#endif
+#ifndef PK_DECODE_NT
+#define PK_DECODE_NT 0
+#endif
+
+namespace pk {
+namespace {
+
+constexpr float kEmptyMax = -1.0e30f;   // running max before any key (finite: 2^(m-m) stays 1)
+
+struct SeqRange {
+  int L;        // admitted keys end (exclusive)
+  int lo;       // admitted keys begin
+  int first;    // first partition index touched
+  int nparts;   // partitions touched (0 when L == 0)
+};
+
+__device__ __forceinline__ SeqRange seq_range(const DecodeArgs& a, int b) {
+  SeqRange r;
+  const int cap = min(a.max_blocks_per_seq * a.block_size, a.max_context_len);
+  r.L = min(max(a.context_lens[b], 0), cap);
+  r.lo = a.sliding_window > 0 ? max(0, r.L - a.sliding_window) : 0;
+  r.first = r.lo / a.partition_size;
+  r.nparts = r.L > 0 ? (r.L - 1) / a.partition_size - r.first + 1 : 0;
+  // The host plan sizes num_parts for the worst sequence; the clamp only keeps
+  // workspace indexing in bounds should a caller break that contract.
+  r.nparts = min(r.nparts, a.num_parts);
+  return r;
+}
+
+template <int NL>
+struct ChunkRegs {
+  uint4 k[NL];
+  uint4 v[NL];
+  bool ok;
+};
+
+__device__ __forceinline__ uint4 load16(const uint4* p) {
+#if PK_DECODE_NT
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
+}
+
+// Chunk of 4*NL tokens starting at logical position `base` (a multiple of
+// 4*NL that divides block_size, so the chunk lies in one cache block).
+template <int NL>
+__device__ __forceinline__ void load_chunk(ChunkRegs<NL>& c, const DecodeArgs& a,
+                                           const int32_t* bt, const uint4* kbase,
+                                           const uint4* vbase, int64_t tok_stride,
+                                           int64_t blk_stride, int base) {
+  const int lb = base / a.block_size;
+  int blk = bt[lb];
+  c.ok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
+  blk = c.ok ? blk : 0;
+  const int64_t off = static_cast<int64_t>(blk) * blk_stride +
+                      static_cast<int64_t>(base - lb * a.block_size) * tok_stride;
+#pragma unroll
+  for (int k = 0; k < NL; ++k) c.k[k] = load16(kbase + off + 4 * k * tok_stride);
+#pragma unroll
+  for (int k = 0; k < NL; ++k) c.v[k] = load16(vbase + off + 4 * k * tok_stride);
+}
+
+template <int G, int NW, int NL>
+__global__ void __launch_bounds__(NW * kWave)
+decode_partition_kernel(DecodeArgs a) {
+  constexpr int CT = 4 * NL;   // tokens per chunk
+  const int lane = threadIdx.x & (kWave - 1);
+  // Wave-uniform by construction; readfirstlane lets the compiler keep the
+  // chunk walk (and its block-table reads) in scalar registers, so a table
+  // read never waits behind the vector loads already in flight.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int row = lane >> 4;   // which of the 4 tokens of a load
+  const int col = lane & 15;   // which 16-byte column of the head row
+  const int b = blockIdx.z;
+  const int g = blockIdx.y;
+  const int pi = blockIdx.x;
+  const int hq = a.num_kv_heads * G;
+  const SeqRange r = seq_range(a, b);
+  uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(b) * hq + g * G) * kHeadDim;
+
+  if (r.nparts == 0) {
+    if (pi == 0)
+      for (int o = threadIdx.x; o < G * kHeadDim; o += NW * kWave) out[o] = 0;
+    return;
+  }
+  if (pi >= r.nparts) return;
+  const int p = r.first + pi;
+  const int t0 = max(p * a.partition_size, r.lo);
+  const int t1 = min((p + 1) * a.partition_size, r.L);
+
+  float qf[G][8];
+  {
+    const uint4* qv = static_cast<const uint4*>(a.q) + (static_cast<int64_t>(b) * hq + g * G) * 16 + col;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      unpack8(qv[h * 16], qf[h]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[h][e] *= a.scale_log2;
+    }
+  }
+
+  const int64_t tok_stride = static_cast<int64_t>(a.num_kv_heads) * 16;  // uint4 per slot
+  const int64_t blk_stride = tok_stride * a.block_size;
+  const uint4* kbase = static_cast<const uint4*>(a.k_cache) + g * 16 + col + row * tok_stride;
+  const uint4* vbase = static_cast<const uint4*>(a.v_cache) + g * 16 + col + row * tok_stride;
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
+
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kEmptyMax;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+
+  // Consume one chunk held in registers (scores, online softmax, P.V).
+  auto consume = [&](const ChunkRegs<NL>& c, int base) {
+    float s[NL][G];
+    bool valid[NL];
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int t = base + 4 * k + row;
+      valid[k] = c.ok && t >= t0 && t < t1;
+      float kf[8];
+      unpack8(c.k[k], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float x = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x = fmaf(qf[h][e], kf[e], x);
+        x = row16_sum(x);
+        s[k][h] = valid[k] ? x : -INFINITY;
+      }
+    }
+    float pw[NL][G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float cm = s[0][h];
+#pragma unroll
+      for (int k = 1; k < NL; ++k) cm = fmaxf(cm, s[k][h]);
+      const float mn = fmaxf(m[h], cm);
+      const float alpha = fast_exp2(m[h] - mn);
+      m[h] = mn;
+      float sum = 0.f;
+#pragma unroll
+      for (int k = 0; k < NL; ++k) {
+        pw[k][h] = fast_exp2(s[k][h] - mn);
+        sum += pw[k][h];
+      }
+      l[h] = fmaf(l[h], alpha, sum);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+    }
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      // Masked tokens get weight 0; their V words are zeroed too so that
+      // stale cache contents (possibly NaN patterns) cannot leak in.
+      const uint4 vw = valid[k] ? c.v[k] : make_uint4(0, 0, 0, 0);
+      float vf[8];
+      unpack8(vw, vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw[k][h], vf[e], acc[h][e]);
+    }
+  };
+
+  // Two register buffers in ping-pong: the loads of the next chunk are in
+  // flight while the current one is consumed, with no register copies.  The
+  // prefetch is unconditional (past the end it re-reads the current chunk, an
+  // in-bounds cache hit): a conditional load would make the wait counters
+  // assume the worst case at the merge and stall on the prefetch itself.
+  const int step = NW * CT;
+  int b0 = (t0 / CT) * CT + wave * CT;
+  if (b0 < t1) {
+    ChunkRegs<NL> ca, cb;
+    load_chunk<NL>(ca, a, bt, kbase, vbase, tok_stride, blk_stride, b0);
+    while (true) {
+      const int b1 = b0 + step;
+      load_chunk<NL>(cb, a, bt, kbase, vbase, tok_stride, blk_stride, b1 < t1 ? b1 : b0);
+      consume(ca, b0);
+      if (b1 >= t1) break;
+      const int b2 = b1 + step;
+      load_chunk<NL>(ca, a, bt, kbase, vbase, tok_stride, blk_stride, b2 < t1 ? b2 : b1);
+      consume(cb, b1);
+      if (b2 >= t1) break;
+      b0 = b2;
+    }
+  }
+
+  // Merge the 4 rows of the wavefront (lanes l, l^16, l^32, l^48 share a column).
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mx = fmaxf(m[h], shfl_xor(m[h], 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float f = fast_exp2(m[h] - mx);
+    float lh = l[h] * f;
+    lh += shfl_xor(lh, 16);
+    lh += shfl_xor(lh, 32);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = acc[h][e] * f;
+      x += shfl_xor(x, 16);
+      x += shfl_xor(x, 32);
+      acc[h][e] = x;
+    }
+    m[h] = mx;
+    l[h] = lh;
+  }
+
+  // Merge the wavefronts through LDS; one thread per (head, dim) output.
+  __shared__ float s_acc[NW][G][kHeadDim];
+  __shared__ float s_m[NW][G];
+  __shared__ float s_l[NW][G];
+  if (row == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_acc[wave][h][col * 8 + e] = acc[h][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s_m[wave][h] = m[h];
+      s_l[wave][h] = l[h];
+    }
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < G * kHeadDim; o += NW * kWave) {
+    const int h = o / kHeadDim;
+    const int d = o % kHeadDim;
+    float mx = s_m[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, s_m[w][h]);
+    float ls = 0.f, av = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = fast_exp2(s_m[w][h] - mx);
+      ls = fmaf(s_l[w][h], f, ls);
+      av = fmaf(s_acc[w][h][d], f, av);
+    }
+    if (r.nparts == 1) {
+      out[o] = static_cast<uint16_t>(f32_to_bf16_bits(ls > 0.f ? av / ls : 0.f));
+    } else {
+      const int64_t slot = (static_cast<int64_t>(b) * hq + g * G + h) * a.num_parts + pi;
+      a.ws_acc[slot * kHeadDim + d] = av;
+      if (d == 0) {
+        a.ws_ml[slot * 2] = mx;
+        a.ws_ml[slot * 2 + 1] = ls;
+      }
+    }
+  }
+}
+
+// Merge the partitions of every sequence that has more than one.
+template <int G>
+__global__ void __launch_bounds__(G * kHeadDim)
+decode_combine_kernel(DecodeArgs a) {
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  const SeqRange r = seq_range(a, b);
+  if (r.nparts <= 1) return;   // written directly by the partition kernel
+  const int hq = a.num_kv_heads * G;
+  const int h = threadIdx.x / kHeadDim;
+  const int d = threadIdx.x % kHeadDim;
+  const int64_t head = static_cast<int64_t>(b) * hq + g * G + h;
+  const float* ml = a.ws_ml + head * a.num_parts * 2;
+  const float* acc = a.ws_acc + head * a.num_parts * kHeadDim + d;
+  // One online pass; each step's loads do not depend on the running state,
+  // so the unrolled loads are all in flight together.
+  float mx = kEmptyMax, ls = 0.f, av = 0.f;
+#pragma unroll 4
+  for (int p = 0; p < r.nparts; ++p) {
+    const float mp = ml[2 * p];
+    const float lp = ml[2 * p + 1];
+    const float ap = acc[p * kHeadDim];
+    const float mn = fmaxf(mx, mp);
+    const float fo = fast_exp2(mx - mn);
+    const float fn = fast_exp2(mp - mn);
+    ls = ls * fo + lp * fn;
+    av = av * fo + ap * fn;
+    mx = mn;
+  }
+  static_cast<uint16_t*>(a.out)[head * kHeadDim + d] =
+      static_cast<uint16_t>(f32_to_bf16_bits(ls > 0.f ? av / ls : 0.f));
+}
+
+constexpr int kDecodeWaves = PK_DECODE_WAVES;
+constexpr int kDecodeLoads = PK_DECODE_LOADS;
+
+template <int G>
+hipError_t launch_group(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
+  // Chunks must not straddle a cache block: fall back to 16-token chunks when
+  // block_size is not a multiple of the wider chunk.
+  if (kDecodeLoads > 4 && a.block_size % (4 * kDecodeLoads) == 0) {
+    hipLaunchKernelGGL((decode_partition_kernel<G, kDecodeWaves, kDecodeLoads>), grid,
+                       dim3(kDecodeWaves * kWave), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_partition_kernel<G, kDecodeWaves, 4>), grid,
+                       dim3(kDecodeWaves * kWave), 0, stream, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_parts <= 1) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<G>), dim3(a.num_kv_heads, a.num_seqs),
+                     dim3(G * kHeadDim), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_seqs == 0) return hipSuccess;
+  switch (a.group) {
+    case 1: return launch_group<1>(a, stream);
+    case 2: return launch_group<2>(a, stream);
+    case 4: return launch_group<4>(a, stream);
+    case 8: return launch_group<8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pk

@@ -22,3 +22,13 @@ def gpu_lib():
         pytest.skip("no GPU")
     import paged_kv_cache_236_amd as pk
     return pk
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU test on the real stderr before it runs, so a run that
+    dies mid-test still says which case it was in."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

@@ -1,0 +1,179 @@
+"""GPU parity of the varlen prefill over a cached prefix (through the C ABI)
+against the CPU oracle: the named 16-sequence workload in full, and edge
+cases (ragged tails, prefixes not aligned to tiles, windows, head groups,
+block sizes, empty sequences, sentinel table padding)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from workloads import bits_of, to_torch
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+
+
+def assert_close(got, ref, rows=None, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
+    g = got.detach().float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        g, ref = g[rows], ref[rows]
+    assert np.isfinite(g).all()
+    err = np.abs(g - ref)
+    assert err.max() <= max_abs and err.mean() <= mean_abs, (float(err.max()), float(err.mean()))
+
+
+def prefill_case(seed, shapes, bs=64, hq=16, hkv=8, window=0, spare=2, mb=None):
+    """shapes: list of (cached prefix P, new tokens Lq).  The cache is N(0,1)
+    everywhere; new K/V are drawn separately and stored at positions P.."""
+    rng = np.random.default_rng(seed)
+    need = [max(1, math.ceil((p + n) / bs)) for p, n in shapes]
+    mb = mb or max(need)
+    nb = len(shapes) * mb + spare
+    tables = rng.permutation(nb)[:len(shapes) * mb].reshape(len(shapes), mb).astype(np.int32)
+    lq = np.array([n for p, n in shapes], np.int32)
+    lk = np.array([p + n for p, n in shapes], np.int32)
+    cuq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cuk = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    total = int(cuq[-1])
+    slots = np.concatenate([W.slot_of(tables, b, np.arange(p, p + n), bs)
+                            for b, (p, n) in enumerate(shapes)] + [np.zeros(0)]).astype(np.int32)
+    return W.PagedInputs(
+        q=W.normal_bf16(rng, (total, hq, 128)),
+        k_cache=W.normal_bf16(rng, (nb, bs, hkv, 128)),
+        v_cache=W.normal_bf16(rng, (nb, bs, hkv, 128)),
+        block_tables=tables, context_lens=lk, block_size=bs, scale=1 / math.sqrt(128),
+        sliding_window=window,
+        key=W.normal_bf16(rng, (total, hkv, 128)), value=W.normal_bf16(rng, (total, hkv, 128)),
+        slot_mapping=slots, cu_seqlens_q=cuq, cu_seqlens_k=cuk)
+
+
+def run_store_prefill(pk, x, t=None, max_seqlen_q=None):
+    t = t or to_torch(x, "cuda")
+    pk.kv_store(t["key"], t["value"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+    msq = max_seqlen_q or int(np.diff(x.cu_seqlens_q).max())
+    out = pk.paged_prefill(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                           t["cu_seqlens_q"], t["cu_seqlens_k"], x.scale,
+                           max_seqlen_q=msq, sliding_window=x.sliding_window)
+    return out, t
+
+
+def oracle_prefill(x):
+    kc, vc = oracle.kv_store(x.k_cache, x.v_cache, x.key, x.value, x.slot_mapping)
+    return oracle.paged_prefill(x.q, kc, vc, x.block_tables, x.cu_seqlens_q, x.cu_seqlens_k,
+                                x.scale, x.sliding_window), kc, vc
+
+
+def test_prefix_prefill_workload(gpu_lib):
+    """16 seqs, new U{64..512}, prefix 0-2 full 256-token blocks, block 256."""
+    x = W.prefix_prefill()
+    out, t = run_store_prefill(gpu_lib, x)
+    ref, kc, vc = oracle_prefill(x)
+    assert np.array_equal(bits_of(t["k_cache"]), kc)
+    assert np.array_equal(bits_of(t["v_cache"]), vc)
+    assert_close(out, ref)
+
+
+SHAPES = [(0, 1), (0, 63), (0, 64), (0, 65), (100, 1), (100, 37), (5, 130), (256, 200),
+          (0, 300), (513, 64)]
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
+def test_prefill_shapes_block_sizes(gpu_lib, bs):
+    x = prefill_case([41, bs], SHAPES, bs=bs)
+    out, _ = run_store_prefill(gpu_lib, x)
+    assert_close(out, oracle_prefill(x)[0])
+
+
+@pytest.mark.parametrize("window", [1, 17, 64, 100, 256])
+def test_prefill_window(gpu_lib, window):
+    x = prefill_case([42, window], SHAPES, bs=32, window=window)
+    out, _ = run_store_prefill(gpu_lib, x)
+    assert_close(out, oracle_prefill(x)[0])
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 8), (64, 8), (4, 2)])
+def test_prefill_group_sizes(gpu_lib, hq, hkv):
+    x = prefill_case([43, hq, hkv], [(0, 40), (70, 90), (3, 129)], bs=32, hq=hq, hkv=hkv)
+    out, _ = run_store_prefill(gpu_lib, x)
+    assert_close(out, oracle_prefill(x)[0])
+
+
+def test_prefill_empty_sequences(gpu_lib):
+    """Sequences with no new tokens own no output rows; neighbours are exact."""
+    x = prefill_case([44], [(10, 0), (0, 50), (64, 0), (30, 70)], bs=16)
+    out, _ = run_store_prefill(gpu_lib, x)
+    assert_close(out, oracle_prefill(x)[0])
+
+
+def test_prefill_single_token_equals_decode(gpu_lib):
+    """Lq = 1 after a prefix of L-1 tokens is one decode step."""
+    x = prefill_case([45], [(0, 1), (99, 1), (700, 1), (255, 1)], bs=64)
+    out, t = run_store_prefill(gpu_lib, x)
+    dec = gpu_lib.paged_decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                               torch.from_numpy(x.context_lens).cuda(), x.scale,
+                               max_context_len=int(x.context_lens.max()))
+    ref = oracle_prefill(x)[0]
+    assert_close(out, ref)
+    assert_close(dec, ref)
+
+
+def test_prefill_chunked_matches_whole(gpu_lib):
+    """Two chunks (the second one over a prefix that includes the first) give
+    the same rows as one pass, within the bf16 bar."""
+    whole = prefill_case([46], [(0, 200), (64, 150)], bs=32)
+    out_whole, t = run_store_prefill(gpu_lib, whole)
+    c = [80, 33]
+    rows1 = np.concatenate([np.arange(0, c[0]), np.arange(200, 200 + c[1])])
+    rows2 = np.concatenate([np.arange(c[0], 200), np.arange(200 + c[1], 350)])
+    for rows, cuq, cuk in (
+            (rows1, [0, c[0], c[0] + c[1]], [0, c[0], c[0] + 64 + c[1]]),
+            (rows2, [0, 200 - c[0], 350 - c[0] - c[1]], [0, 200, 200 + 214])):
+        q = t["q"][torch.from_numpy(rows).cuda()].contiguous()
+        out = gpu_lib.paged_prefill(q, t["k_cache"], t["v_cache"], t["block_tables"],
+                                    torch.tensor(cuq, dtype=torch.int32, device="cuda"),
+                                    torch.tensor(cuk, dtype=torch.int32, device="cuda"),
+                                    whole.scale, max_seqlen_q=int(np.diff(cuq).max()))
+        d = (out.float() - out_whole[torch.from_numpy(rows).cuda()].float()).abs()
+        assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3
+
+
+def test_prefill_permutation_bit_exact_and_deterministic(gpu_lib):
+    x = prefill_case([47], [(100, 120), (0, 77)], bs=32, spare=5)
+    out1, t = run_store_prefill(gpu_lib, x)
+    out1b = gpu_lib.paged_prefill(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                  t["cu_seqlens_q"], t["cu_seqlens_k"], x.scale, max_seqlen_q=120)
+    assert torch.equal(out1.view(torch.int16), out1b.view(torch.int16))
+    perm = np.random.default_rng(48).permutation(x.k_cache.shape[0])
+    y = W.PagedInputs(**{**x.__dict__})
+    y.k_cache = np.empty_like(x.k_cache)
+    y.v_cache = np.empty_like(x.v_cache)
+    y.k_cache[perm] = x.k_cache
+    y.v_cache[perm] = x.v_cache
+    y.block_tables = perm[x.block_tables].astype(np.int32)
+    y.slot_mapping = (perm[x.slot_mapping // 32] * 32 + x.slot_mapping % 32).astype(np.int32)
+    out2, _ = run_store_prefill(gpu_lib, y)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+def test_prefill_sentinel_padding_never_read(gpu_lib):
+    x = prefill_case([49], [(10, 30), (0, 5)], bs=16, mb=8)
+    out1, _ = run_store_prefill(gpu_lib, x)
+    y = W.PagedInputs(**{**x.__dict__})
+    y.block_tables = x.block_tables.copy()
+    for b, L in enumerate(x.context_lens):
+        y.block_tables[b, math.ceil(L / 16):] = np.iinfo(np.int32).max
+    out2, _ = run_store_prefill(gpu_lib, y)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+def test_prefill_long_prefix_window(gpu_lib):
+    """A long cached prefix (1800 tokens) with a window of 256 and with none."""
+    for window in (0, 256):
+        x = prefill_case([50, window], [(1800, 300), (1000, 17)], bs=256, window=window)
+        out, _ = run_store_prefill(gpu_lib, x)
+        assert_close(out, oracle_prefill(x)[0])

@@ -121,6 +121,7 @@ def decode_inputs(workload_id: int, num_seqs: int, ctx_lo: int, ctx_hi: int,
                   block_size: int, *, blocks_per_seq: Optional[int] = None,
                   layer: int = 0, q_mul: float = 1.0, scale: Optional[float] = None,
                   sliding_window: int = 0, store_new_token: bool = False,
+                  with_caches: bool = True,
                   heads=(NUM_Q_HEADS, NUM_KV_HEADS, HEAD_DIM)) -> PagedInputs:
     """Decode batch: one query token per sequence over a paged cache.
 
@@ -129,7 +130,8 @@ def decode_inputs(workload_id: int, num_seqs: int, ctx_lo: int, ctx_hi: int,
     permutation of all blocks.  With ``store_new_token`` the token at position
     L_b - 1 is drawn separately and stored through slot_mapping before
     attention.  The lengths and tables depend only on ``workload_id``; the
-    values also on ``layer``.
+    values also on ``layer``.  With ``with_caches=False`` the caches are left
+    empty (shape [0, ...]) for drawing on the GPU with ``device_caches``.
     """
     hq, hkv, d = heads
     if blocks_per_seq is None:
@@ -140,8 +142,9 @@ def decode_inputs(workload_id: int, num_seqs: int, ctx_lo: int, ctx_hi: int,
     nb = num_seqs * blocks_per_seq
     vals = rng_for(workload_id, 1, layer)
     q = normal_bf16(vals, (num_seqs, hq, d), mul=q_mul)
-    kc = normal_bf16(vals, (nb, block_size, hkv, d))
-    vc = normal_bf16(vals, (nb, block_size, hkv, d))
+    cshape = (nb if with_caches else 0, block_size, hkv, d)
+    kc = normal_bf16(vals, cshape)
+    vc = normal_bf16(vals, cshape)
     out = PagedInputs(q=q, k_cache=kc, v_cache=vc, block_tables=tables,
                       context_lens=ctx, block_size=block_size,
                       scale=(1.0 / math.sqrt(d)) if scale is None else scale,
@@ -235,6 +238,36 @@ def long_decode(sliding_window: int = 0, num_seqs: int = 64) -> PagedInputs:
                          sliding_window=sliding_window)
 
 
+LONG_DECODE_BLOCKS = 64 * 32
+
+
+def long_decode_meta(sliding_window: int = 0) -> PagedInputs:
+    """The long-context workload without its 2 GiB of caches (q, tables and
+    lengths only); draw the caches with long_decode_device_caches()."""
+    return decode_inputs(LONG_DECODE, 64, 4096, 8192, 256,
+                         sliding_window=sliding_window, with_caches=False)
+
+
+def long_decode_device_caches(device):
+    return device_caches(LONG_DECODE, LONG_DECODE_BLOCKS, 256, device)
+
+
+def deep_decode_layer_meta(layer: int) -> PagedInputs:
+    """One layer of the 28-layer workload without its caches."""
+    return decode_inputs(DEEP_DECODE, 64, 512, 1024, 256, layer=layer,
+                         q_mul=1.0 / math.sqrt(HEAD_DIM), scale=1.0,
+                         store_new_token=True, with_caches=False)
+
+
+def device_caches(workload_id: int, num_blocks: int, block_size: int, device, layer: int = 0,
+                  heads=(NUM_Q_HEADS, NUM_KV_HEADS, HEAD_DIM)):
+    """(k_cache, v_cache) bf16 N(0,1) [num_blocks, block_size, Hkv, d] drawn on
+    the GPU (see device_normal_bf16)."""
+    shape = (num_blocks, block_size, heads[1], heads[2])
+    return (device_normal_bf16(shape, [workload_id, 2, layer, 0], device),
+            device_normal_bf16(shape, [workload_id, 2, layer, 1], device))
+
+
 # --- device-side drawing for the full-size workloads ---------------------------
 
 def device_normal_bf16(shape, seed_words, device, mul: float = 1.0):
@@ -253,3 +286,34 @@ def device_normal_bf16(shape, seed_words, device, mul: float = 1.0):
     if mul != 1.0:
         x.mul_(mul)
     return x.to(torch.bfloat16)
+
+
+def to_torch(x: PagedInputs, device) -> dict:
+    """The same arrays as torch tensors on ``device`` (bf16 bits reinterpreted
+    as torch.bfloat16, index arrays as int32)."""
+    import torch
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+    t = {
+        "q": bf(x.q), "k_cache": bf(x.k_cache), "v_cache": bf(x.v_cache),
+        "block_tables": i32(x.block_tables), "context_lens": i32(x.context_lens),
+    }
+    if x.key is not None:
+        t["key"] = bf(x.key)
+        t["value"] = bf(x.value)
+        t["slot_mapping"] = i32(x.slot_mapping)
+    if x.cu_seqlens_q is not None:
+        t["cu_seqlens_q"] = i32(x.cu_seqlens_q)
+        t["cu_seqlens_k"] = i32(x.cu_seqlens_k)
+    return t
+
+
+def bits_of(t) -> np.ndarray:
+    """A torch bf16 tensor (any device) -> numpy uint16 bit patterns."""
+    import torch
+    return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
