@@ -2,17 +2,19 @@
 """Benchmark of the paged KV-cache attention path on one MI355X.
 
 A step is one decode step of a 28-layer Qwen3-0.6B-shaped model at
-concurrency 64: for each layer, store the 64 new tokens' K/V (kv_store) and
-run decode attention over the paged cache (paged_decode: split-K partition
-kernel + combine kernel).  Workload: 64 seqs, context U{512..1024}, block 256,
+concurrency 64: for each layer, store the 64 new tokens' K/V and run decode
+attention over the paged cache, in one launch per layer (paged_decode_store;
+`--unfused` runs kv_store + paged_decode instead).  Workload: 64 seqs, context U{512..1024}, block 256,
 16 q heads / 8 KV heads / head_dim 128, bf16, 28 independent layer caches
 (7 GiB), q pre-scaled.  Inputs are synthetic, drawn with fixed seeds, resident
 in HBM before timing starts.  By default the step is captured once in a HIP
 graph and replayed (the pages' decode runs with graph replay); the eager rate
 is reported next to it.
 
-The varlen prefill over a cached prefix (16 seqs, new U{64..512}, prefix 0-2
-blocks) is timed as a second leg and reported as MFMA utilisation.
+Further legs, each timed alone: the varlen prefill over a cached prefix (16
+seqs, new U{64..512}, prefix 0-2 blocks; MFMA utilisation), the long-context
+decode (64 seqs, context U{4096..8192}, with and without a 256-token window;
+HBM fraction) and the two small decode workloads (latency).
 
 Prints ONE JSON line.  `value` = algorithmic bytes of the step (K/V read by
 decode for the admitted positions, q, out, block tables, kv_store traffic) /
@@ -46,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--layers", type=int, default=28)
+    ap.add_argument("--unfused", action="store_true")
+    ap.add_argument("--no-legs", action="store_true")
     return ap.parse_args()
 
 
@@ -122,10 +126,18 @@ def main():
         pk.paged_decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
                         scale, max_context_len=maxctx, out=t["out"], workspace=ws)
 
+    def fused(t):
+        pk.paged_decode_store(t["q"], t["key"], t["value"], t["k_cache"], t["v_cache"],
+                              t["block_tables"], t["context_lens"], scale, max_context_len=maxctx,
+                              out=t["out"], workspace=ws)
+
     def step():
         for t in layers:
-            store(t)
-            decode(t)
+            if args.unfused:
+                store(t)
+                decode(t)
+            else:
+                fused(t)
 
     def timed(fn, steps):
         torch.cuda.synchronize()
@@ -161,32 +173,32 @@ def main():
     else:
         ms_per_step = max(eager_ms, eager_wall_ms)
 
-    # ---- per-kernel duration of the decode call (events on its stream) ------
-    # A spin kernel first gives the host a head start, so the events time GPU
-    # work back to back, not host launch gaps.
-    torch.cuda.synchronize()
-    torch.cuda._sleep(50_000_000)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in layers]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in layers]
-    for t, s, e in zip(layers, starts, ends):
-        s.record(stream)
-        decode(t)
-        e.record(stream)
-    torch.cuda.synchronize()
-    dec_us = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / len(layers) * 1e3
-    torch.cuda._sleep(50_000_000)
-    for t, s, e in zip(layers, starts, ends):
-        s.record(stream)
-        store(t)
-        e.record(stream)
-    torch.cuda.synchronize()
-    store_us = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / len(layers) * 1e3
+    # ---- per-launch duration of each call (events on its stream) ------------
+    def per_call_us(fn):
+        # A spin kernel first gives the host a head start, so the events time
+        # GPU work back to back, not host launch gaps.
+        torch.cuda.synchronize()
+        torch.cuda._sleep(20_000_000)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in layers]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in layers]
+        for t, s0, e0 in zip(layers, starts, ends):
+            s0.record(stream)
+            fn(t)
+            e0.record(stream)
+        torch.cuda.synchronize()
+        return sum(s0.elapsed_time(e0) for s0, e0 in zip(starts, ends)) / len(layers) * 1e3
+
+    fused_us = per_call_us(fused)
+    dec_us = per_call_us(decode)
+    store_us = per_call_us(store)
 
     dbytes = decode_bytes(ctx, bs, hq, hkv, d)
     sbytes = store_bytes(64, hkv, d)
     step_bytes = nl * (dbytes + sbytes)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dec_gbs = dbytes / (dec_us * 1e-6) / 1e9
+    launch_us = dec_us if args.unfused else fused_us
+    launch_bytes = dbytes if args.unfused else dbytes + sbytes
+    dec_gbs = launch_bytes / (launch_us * 1e-6) / 1e9
 
     result = {
         "metric": METRIC,
@@ -202,7 +214,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "decode step, 28 layers x (kv_store + paged_decode), c=64",
+            "workload": ("decode step, 28 layers x (kv_store + paged_decode), c=64" if args.unfused
+                         else "decode step, 28 layers x paged_decode_store (store + attend), c=64"),
             "num_seqs": 64, "context_lens": "U{512..1024}", "block_size": bs,
             "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d, "layers": nl,
             "mode": args.mode, "partition_size": ps, "partitions_per_seq": nparts,
@@ -211,18 +224,19 @@ def main():
         "attn_tokens_per_s": round(64 / (ms_per_step * 1e-3), 1),
         "eager_ms_per_step": round(max(eager_ms, eager_wall_ms), 4),
         "roofline": {
-            "kernel": "paged_decode call (decode_partition_kernel + decode_combine_kernel)",
+            "kernel": ("decode_partition_kernel" + ("" if nparts == 1 else " + decode_combine_kernel")
+                       + ("" if args.unfused else " (fused store)")),
             "bound": "hbm",
             "achieved": round(dec_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "bytes_per_launch": dbytes,
-            "us_per_launch": round(dec_us, 2),
+            "bytes_per_launch": launch_bytes,
+            "us_per_launch": round(launch_us, 2),
         },
-        "kv_store": {"us_per_launch": round(store_us, 2), "bytes_per_launch": sbytes,
-                     "GB/s": round(sbytes / (store_us * 1e-6) / 1e9, 1)},
+        "unfused": {"paged_decode_us": round(dec_us, 2), "kv_store_us": round(store_us, 2),
+                    "paged_decode_GBps": round(dbytes / (dec_us * 1e-6) / 1e9, 1)},
     }
 
     # ---- prefill leg ----------------------------------------------------------
@@ -232,12 +246,79 @@ def main():
         except pk.PagedKVError as e:
             result["prefill"] = {"error": str(e)}
 
+    if not args.no_legs:
+        del layers
+        result["long_decode"] = long_leg(args, pk, W, dev, stream)
+        result["small_decode"] = small_leg(args, pk, W, dev, stream)
+
     # ---- CPU baseline: the oracle on a bounded sample -------------------------
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W, dbytes)
 
-    del layers
     print(json.dumps(result), flush=True)
+
+
+def time_call(fn, stream, n):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(20_000_000)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3
+
+
+def long_leg(args, pk, W, dev, stream):
+    """64 seqs, context U{4096..8192}, block 256, 2 GiB cache: full and window 256."""
+    import torch
+    res = {}
+    kc, vc = W.long_decode_device_caches(dev)
+    for window in (0, 256):
+        m = W.long_decode_meta(window)
+        t = W.to_torch(m, dev)
+        mcl = int(m.context_lens.max())
+        out = torch.empty_like(t["q"])
+        ps, nparts = pk.decode_plan(64, 8, mcl, window)
+
+        def run():
+            pk.paged_decode(t["q"], kc, vc, t["block_tables"], t["context_lens"], m.scale,
+                            sliding_window=window, max_context_len=mcl, out=out)
+        us = time_call(run, stream, 10)
+        nbytes = decode_bytes(m.context_lens, 256, 16, 8, 128, window)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res["window_256" if window else "full"] = {
+            "us_per_launch": round(us, 2), "bytes_per_launch": nbytes, "GB/s": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "partition_size": ps, "partitions_per_seq": nparts}
+    return res
+
+
+def small_leg(args, pk, W, dev, stream):
+    """8 seqs block 16 (decode), and 16 seqs block 256 (store + decode in one launch)."""
+    import torch
+    res = {}
+    x = W.small_decode()
+    t = W.to_torch(x, dev)
+    mcl = x.max_context_len
+    us = time_call(lambda: pk.paged_decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                           t["context_lens"], x.scale, max_context_len=mcl),
+                   stream, 50)
+    res["8seq_block16"] = {"us_per_launch": round(us, 2),
+                           "bytes_per_launch": decode_bytes(x.context_lens, 16, 16, 8, 128)}
+    y = W.store_decode()
+    t = W.to_torch(y, dev)
+    mcl = y.max_context_len
+    us = time_call(lambda: pk.paged_decode_store(t["q"], t["key"], t["value"], t["k_cache"],
+                                                 t["v_cache"], t["block_tables"], t["context_lens"],
+                                                 y.scale, max_context_len=mcl), stream, 50)
+    res["16seq_block256_store"] = {"us_per_launch": round(us, 2),
+                                   "bytes_per_launch": decode_bytes(y.context_lens, 256, 16, 8, 128)
+                                   + store_bytes(16, 8, 128)}
+    return res
 
 
 def prefill_leg(args, pk, W, dev, stream):

@@ -150,6 +150,33 @@ pk_status pk_paged_decode(void* out, const void* q,
                           void* stream);
 
 /*
+ * pk_paged_decode_store — the decode step's store and attention in one
+ * launch: for every sequence b with L_b = context_lens[b] > 0, the new token's
+ * K/V rows k_new[b], v_new[b] (bf16 [num_seqs, num_kv_heads, head_dim]) are
+ * written to the cache slot of position L_b - 1 (found through block_tables,
+ * as the block manager allocated it), and attention is computed exactly as
+ * pk_paged_decode over positions lo..L_b-1 with position L_b - 1 taken from
+ * k_new / v_new.  Results and caches are bit-identical to pk_kv_store with
+ * slot_mapping[b] = slot of position L_b - 1 followed by pk_paged_decode.
+ * (The fused kernel the nano-vllm-sansho README names as an optimization
+ * target, "Sansho Serving Roofline Anchors".)  Other arguments, workspace
+ * sizing and errors as pk_paged_decode.  A block-table entry outside the cache
+ * for position L_b - 1 means nothing is stored for that sequence.
+ */
+pk_status pk_paged_decode_store(void* out, const void* q,
+                                const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache,
+                                int32_t num_blocks, int32_t block_size,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t max_context_len,
+                                float scale, int32_t sliding_window,
+                                int32_t partition_size_request,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * pk_paged_prefill — variable-length causal attention for the new tokens of
  * several sequences whose prefix may already be cached (prefix caching:
  * nano-vllm-sansho README "Key Features"; prefill and decode as separate

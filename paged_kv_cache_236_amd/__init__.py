@@ -19,7 +19,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "LIB_PATH", "PagedKVError", "version", "kv_store", "paged_decode", "paged_prefill",
+    "LIB_PATH", "PagedKVError", "version", "kv_store", "paged_decode", "paged_decode_store",
+    "paged_prefill",
     "decode_plan", "decode_workspace_size",
 ]
 
@@ -52,6 +53,9 @@ _lib.pk_paged_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i
 _lib.pk_paged_decode.restype = ctypes.c_int
 _lib.pk_paged_decode.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p, _i32,
                                  _i32, _i32, _f32, _i32, _i32, _p, _sz, _p]
+_lib.pk_paged_decode_store.restype = ctypes.c_int
+_lib.pk_paged_decode_store.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p,
+                                       _i32, _i32, _i32, _f32, _i32, _i32, _p, _sz, _p]
 _lib.pk_paged_prefill.restype = ctypes.c_int
 _lib.pk_paged_prefill.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p, _p,
                                   _i32, _i32, _i32, _i32, _f32, _i32, _p]
@@ -150,18 +154,9 @@ def _workspace(device, nbytes: int) -> Optional[torch.Tensor]:
     return ws
 
 
-def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                 block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, *,
-                 sliding_window: int = 0, max_context_len: Optional[int] = None,
-                 out: Optional[torch.Tensor] = None, partition_size: int = 0,
-                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Decode attention: q [num_seqs, num_q_heads, 128] bf16 -> out (same shape).
-
-    max_context_len defaults to context_lens.max() (a device-to-host sync);
-    pass it to keep the call asynchronous.
-    """
+def _decode_common(q, k_cache, v_cache, block_tables, context_lens, sliding_window,
+                   max_context_len, out, partition_size, workspace):
     nb, bs, hkv, d = _cache_dims(k_cache, v_cache)
-    dev = q.device
     if q.dim() != 3:
         raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
     nseq, hq, qd = (int(x) for x in q.shape)
@@ -175,17 +170,60 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         out = torch.empty_like(q)
     elif out.shape != q.shape:
         raise ValueError("out must have q's shape")
+    dev = q.device
     need = decode_workspace_size(nseq, hq, hkv, d, max_context_len, sliding_window, partition_size)
     if workspace is None:
         workspace = _workspace(dev, need)
     ws_ptr = _dev(workspace, "workspace", torch.uint8, dev) if workspace is not None else None
     ws_bytes = int(workspace.numel()) if workspace is not None else 0
+    return (nb, bs, hkv, d, nseq, hq, max_context_len, out, ws_ptr, ws_bytes)
+
+
+def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, *,
+                 sliding_window: int = 0, max_context_len: Optional[int] = None,
+                 out: Optional[torch.Tensor] = None, partition_size: int = 0,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention: q [num_seqs, num_q_heads, 128] bf16 -> out (same shape).
+
+    max_context_len defaults to context_lens.max() (a device-to-host sync);
+    pass it to keep the call asynchronous.
+    """
+    dev = q.device
+    nb, bs, hkv, d, nseq, hq, mcl, out, ws_ptr, ws_bytes = _decode_common(
+        q, k_cache, v_cache, block_tables, context_lens, sliding_window, max_context_len, out,
+        partition_size, workspace)
     _check(_lib.pk_paged_decode(
         _dev(out, "out", torch.bfloat16, dev), _dev(q, "q", torch.bfloat16, dev),
         _dev(k_cache, "k_cache", torch.bfloat16, dev), _dev(v_cache, "v_cache", torch.bfloat16, dev),
         nb, bs, hkv, d,
         _dev(block_tables, "block_tables", torch.int32, dev), int(block_tables.shape[1]),
-        _dev(context_lens, "context_lens", torch.int32, dev), nseq, hq, max_context_len,
+        _dev(context_lens, "context_lens", torch.int32, dev), nseq, hq, mcl,
+        float(scale), sliding_window, partition_size, ws_ptr, ws_bytes, _stream(dev)))
+    return out
+
+
+def paged_decode_store(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                       k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                       context_lens: torch.Tensor, scale: float, *, sliding_window: int = 0,
+                       max_context_len: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                       partition_size: int = 0,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Store the new token k_new/v_new [num_seqs, num_kv_heads, 128] at position
+    context_lens-1 of each sequence and run decode attention, in one launch."""
+    dev = q.device
+    nb, bs, hkv, d, nseq, hq, mcl, out, ws_ptr, ws_bytes = _decode_common(
+        q, k_cache, v_cache, block_tables, context_lens, sliding_window, max_context_len, out,
+        partition_size, workspace)
+    if k_new.shape != (nseq, hkv, d) or v_new.shape != (nseq, hkv, d):
+        raise ValueError(f"k_new/v_new must be [{nseq}, {hkv}, {d}]")
+    _check(_lib.pk_paged_decode_store(
+        _dev(out, "out", torch.bfloat16, dev), _dev(q, "q", torch.bfloat16, dev),
+        _dev(k_new, "k_new", torch.bfloat16, dev), _dev(v_new, "v_new", torch.bfloat16, dev),
+        _dev(k_cache, "k_cache", torch.bfloat16, dev), _dev(v_cache, "v_cache", torch.bfloat16, dev),
+        nb, bs, hkv, d,
+        _dev(block_tables, "block_tables", torch.int32, dev), int(block_tables.shape[1]),
+        _dev(context_lens, "context_lens", torch.int32, dev), nseq, hq, mcl,
         float(scale), sliding_window, partition_size, ws_ptr, ws_bytes, _stream(dev)))
     return out
 

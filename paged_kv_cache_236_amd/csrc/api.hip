@@ -93,11 +93,21 @@ pk_status plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max_contex
   const int64_t ctx = std::max<int32_t>(max_context_len, 1);
   int64_t ps = request;
   if (ps == 0) {
-    // Largest partition (<= 1024 tokens) that still gives >= 2048 workgroups,
-    // i.e. >= 8 per compute unit, so the 256 CUs stay busy through the tail.
+    // Keys one (sequence, KV head) can attend.
+    const int64_t eff = sliding_window > 0 ? std::min<int64_t>(ctx, sliding_window) : ctx;
     const int64_t pairs = static_cast<int64_t>(std::max(num_seqs, 1)) * num_kv_heads;
-    ps = 1024;
-    while (ps > kPartitionQuantum && pairs * slots_for(ctx, sliding_window, ps) < 2048) ps /= 2;
+    if (pairs >= 256) {
+      // The grid already covers every CU: one partition per pair up to 2048
+      // keys (no combine launch), 2048-key partitions beyond; a window spans
+      // about two partitions of half its size.
+      ps = 64;
+      const int64_t want = sliding_window > 0 ? std::max<int64_t>(eff / 2, 64) : std::min<int64_t>(eff, 2048);
+      while (ps < want) ps *= 2;
+    } else {
+      // Few pairs: split until >= 512 workgroups (2 per CU), 64 keys at least.
+      ps = 2048;
+      while (ps > kPartitionQuantum && pairs * slots_for(ctx, sliding_window, ps) < 512) ps /= 2;
+    }
   }
   const int64_t slots = slots_for(ctx, sliding_window, ps);
   if (slots > 65535) return fail(PK_ERR_UNSUPPORTED, "too many partitions (%lld)", (long long)slots);
@@ -115,6 +125,64 @@ size_t workspace_bytes_for(int32_t num_seqs, int32_t num_q_heads, const Plan& p)
 }
 
 }  // namespace
+
+static pk_status paged_decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                          int32_t head_dim, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                          float scale, int32_t sliding_window, int32_t partition_size_request,
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          const void* k_new, const void* v_new) {
+  pk_status s = check_cache_shape(num_blocks, block_size, num_kv_heads, head_dim);
+  if (s != PK_OK) return s;
+  if ((s = check_heads(num_q_heads, num_kv_heads)) != PK_OK) return s;
+  if (max_blocks_per_seq <= 0)
+    return fail(PK_ERR_INVALID_ARG, "max_blocks_per_seq must be > 0 (got %d)", max_blocks_per_seq);
+  if (!std::isfinite(scale)) return fail(PK_ERR_INVALID_ARG, "scale must be finite");
+  Plan p;
+  if ((s = plan_decode(num_seqs, num_kv_heads, max_context_len, sliding_window,
+                       partition_size_request, &p)) != PK_OK)
+    return s;
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PK_ERR_INVALID_ARG, "null pointer argument");
+  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, p);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PK_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(PK_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  pk::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  const size_t heads = static_cast<size_t>(num_seqs) * num_q_heads * p.num_parts;
+  a.ws_acc = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                            (heads * kHeadDim * sizeof(float) + 255) / 256 * 256)
+                 : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.sliding_window = sliding_window;
+  a.partition_size = p.partition_size;
+  a.num_parts = p.num_parts;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
+  const hipError_t e = pk::launch_paged_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PK_ERR_LAUNCH, "paged_decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 
 extern "C" {
 
@@ -196,51 +264,26 @@ pk_status pk_paged_decode(void* out, const void* q, const void* k_cache, const v
                           int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                           float scale, int32_t sliding_window, int32_t partition_size_request,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  pk_status s = check_cache_shape(num_blocks, block_size, num_kv_heads, head_dim);
-  if (s != PK_OK) return s;
-  if ((s = check_heads(num_q_heads, num_kv_heads)) != PK_OK) return s;
-  if (max_blocks_per_seq <= 0)
-    return fail(PK_ERR_INVALID_ARG, "max_blocks_per_seq must be > 0 (got %d)", max_blocks_per_seq);
-  if (!std::isfinite(scale)) return fail(PK_ERR_INVALID_ARG, "scale must be finite");
-  Plan p;
-  if ((s = plan_decode(num_seqs, num_kv_heads, max_context_len, sliding_window,
-                       partition_size_request, &p)) != PK_OK)
-    return s;
-  if (num_seqs == 0) return ok();
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-    return fail(PK_ERR_INVALID_ARG, "null pointer argument");
-  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, p);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PK_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                workspace ? workspace_bytes : static_cast<size_t>(0));
-  if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
-    return fail(PK_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  pk::DecodeArgs a;
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  const size_t heads = static_cast<size_t>(num_seqs) * num_q_heads * p.num_parts;
-  a.ws_acc = need ? static_cast<float*>(workspace) : nullptr;
-  a.ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                            (heads * kHeadDim * sizeof(float) + 255) / 256 * 256)
-                 : nullptr;
-  a.num_seqs = num_seqs;
-  a.num_kv_heads = num_kv_heads;
-  a.group = num_q_heads / num_kv_heads;
-  a.num_blocks = num_blocks;
-  a.block_size = block_size;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.max_context_len = max_context_len;
-  a.sliding_window = sliding_window;
-  a.partition_size = p.partition_size;
-  a.num_parts = p.num_parts;
-  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
-  const hipError_t e = pk::launch_paged_decode(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(PK_ERR_LAUNCH, "paged_decode launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return paged_decode_impl(out, q, k_cache, v_cache, num_blocks, block_size, num_kv_heads, head_dim,
+                           block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                           max_context_len, scale, sliding_window, partition_size_request,
+                           workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+pk_status pk_paged_decode_store(void* out, const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, int32_t num_blocks,
+                                int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t max_context_len, float scale,
+                                int32_t sliding_window, int32_t partition_size_request,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new))
+    return fail(PK_ERR_INVALID_ARG, "null pointer argument (k_new / v_new)");
+  return paged_decode_impl(out, q, k_cache, v_cache, num_blocks, block_size, num_kv_heads, head_dim,
+                           block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                           max_context_len, scale, sliding_window, partition_size_request,
+                           workspace, workspace_bytes, stream, k_new, v_new);
 }
 
 pk_status pk_paged_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -54,6 +54,13 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 __device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, kWave); }
 
+// a.lo*b.lo + a.hi*b.hi + c for two packed bf16 pairs (fp32 products and sum).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace pk

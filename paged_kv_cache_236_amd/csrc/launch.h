@@ -30,6 +30,8 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const void* k_new;       // bf16 [num_seqs, num_kv_heads, 128]: the token at position L-1, or
+  const void* v_new;       // nullptr (then position L-1 is read from the cache like any other)
   float* ws_acc;           // [num_seqs, num_q_heads, num_parts, 128] fp32 (split only)
   float* ws_ml;            // [num_seqs, num_q_heads, num_parts, 2] fp32 (split only)
   int32_t num_seqs;

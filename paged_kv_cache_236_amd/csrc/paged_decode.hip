@@ -17,8 +17,7 @@
 // inner loop needs no cross-row traffic: q.k is reduced over the row's 16 lanes
 // with DPP moves, everything else is lane-local.  Rows, then wavefronts, are
 // merged only once at the end (shuffles, then LDS).  The next chunk's loads
-// are issued before the current chunk is consumed, so each wavefront keeps two
-// chunks (16 KiB) of loads in flight.
+// are issued before the current chunk is consumed.
 //
 // Scores are kept in the log2 domain: q is pre-multiplied by scale*log2(e) in
 // fp32 and the hardware exp2 is used.
@@ -39,7 +38,10 @@
 #define PK_DECODE_LOADS 4
 #endif
 #ifndef PK_DECODE_NT
-#define PK_DECODE_NT 0
+#define PK_DECODE_NT 1
+#endif
+#ifndef PK_DECODE_DOT2
+#define PK_DECODE_DOT2 1    // q.k with packed bf16 dot products (fp32 products and sums)
 #endif
 
 namespace pk {
@@ -71,7 +73,8 @@ template <int NL>
 struct ChunkRegs {
   uint4 k[NL];
   uint4 v[NL];
-  bool ok;
+  int64_t off;   // offset (16-byte units) of the chunk's first token in the caches
+  bool ok;       // the chunk's block-table entry is a valid block
 };
 
 __device__ __forceinline__ uint4 load16(const uint4* p) {
@@ -85,25 +88,28 @@ __device__ __forceinline__ uint4 load16(const uint4* p) {
 }
 
 // Chunk of 4*NL tokens starting at logical position `base` (a multiple of
-// 4*NL that divides block_size, so the chunk lies in one cache block).
+// 4*NL that divides block_size, so the chunk lies in one cache block).  The
+// table index is clamped into the row, and an entry outside the cache reads
+// block 0 with `ok` false, so every address is in bounds whatever the table
+// holds.
 template <int NL>
 __device__ __forceinline__ void load_chunk(ChunkRegs<NL>& c, const DecodeArgs& a,
                                            const int32_t* bt, const uint4* kbase,
                                            const uint4* vbase, int64_t tok_stride,
                                            int64_t blk_stride, int base) {
-  const int lb = base / a.block_size;
+  const int lb = min(base / a.block_size, a.max_blocks_per_seq - 1);
   int blk = bt[lb];
   c.ok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
   blk = c.ok ? blk : 0;
-  const int64_t off = static_cast<int64_t>(blk) * blk_stride +
-                      static_cast<int64_t>(base - lb * a.block_size) * tok_stride;
+  c.off = static_cast<int64_t>(blk) * blk_stride +
+          static_cast<int64_t>(base - lb * a.block_size) * tok_stride;
 #pragma unroll
-  for (int k = 0; k < NL; ++k) c.k[k] = load16(kbase + off + 4 * k * tok_stride);
+  for (int k = 0; k < NL; ++k) c.k[k] = load16(kbase + c.off + 4 * k * tok_stride);
 #pragma unroll
-  for (int k = 0; k < NL; ++k) c.v[k] = load16(vbase + off + 4 * k * tok_stride);
+  for (int k = 0; k < NL; ++k) c.v[k] = load16(vbase + c.off + 4 * k * tok_stride);
 }
 
-template <int G, int NW, int NL>
+template <int G, int NW, int NL, bool FUSE>
 __global__ void __launch_bounds__(NW * kWave)
 decode_partition_kernel(DecodeArgs a) {
   constexpr int CT = 4 * NL;   // tokens per chunk
@@ -118,9 +124,25 @@ decode_partition_kernel(DecodeArgs a) {
   const int g = blockIdx.y;
   const int pi = blockIdx.x;
   const int hq = a.num_kv_heads * G;
+
+  const int64_t tok_stride = static_cast<int64_t>(a.num_kv_heads) * 16;  // uint4 per slot
+  const int64_t blk_stride = tok_stride * a.block_size;
+  const uint4* kbase = static_cast<const uint4*>(a.k_cache) + g * 16 + col + row * tok_stride;
+  const uint4* vbase = static_cast<const uint4*>(a.v_cache) + g * 16 + col + row * tok_stride;
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
+
+  // Without a window, partition pi starts at pi * partition_size whatever the
+  // sequence length, so the first chunk's table read and K/V loads are issued
+  // together with the context-length read instead of after it (one memory
+  // round trip less before the first bytes arrive).  They are wasted if the
+  // partition turns out to be empty.
+  const bool spec = a.sliding_window == 0;
+  ChunkRegs<NL> ca, cb;
+  if (spec) load_chunk<NL>(ca, a, bt, kbase, vbase, tok_stride, blk_stride,
+                           pi * a.partition_size + wave * CT);
+
   const SeqRange r = seq_range(a, b);
   uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(b) * hq + g * G) * kHeadDim;
-
   if (r.nparts == 0) {
     if (pi == 0)
       for (int o = threadIdx.x; o < G * kHeadDim; o += NW * kWave) out[o] = 0;
@@ -131,6 +153,15 @@ decode_partition_kernel(DecodeArgs a) {
   const int t0 = max(p * a.partition_size, r.lo);
   const int t1 = min((p + 1) * a.partition_size, r.L);
 
+#if PK_DECODE_DOT2
+  // q kept as packed bf16 pairs; the scale is applied to the reduced score.
+  uint4 qp[G];
+  {
+    const uint4* qv = static_cast<const uint4*>(a.q) + (static_cast<int64_t>(b) * hq + g * G) * 16 + col;
+#pragma unroll
+    for (int h = 0; h < G; ++h) qp[h] = qv[h * 16];
+  }
+#else
   float qf[G][8];
   {
     const uint4* qv = static_cast<const uint4*>(a.q) + (static_cast<int64_t>(b) * hq + g * G) * 16 + col;
@@ -141,12 +172,18 @@ decode_partition_kernel(DecodeArgs a) {
       for (int e = 0; e < 8; ++e) qf[h][e] *= a.scale_log2;
     }
   }
+#endif
 
-  const int64_t tok_stride = static_cast<int64_t>(a.num_kv_heads) * 16;  // uint4 per slot
-  const int64_t blk_stride = tok_stride * a.block_size;
-  const uint4* kbase = static_cast<const uint4*>(a.k_cache) + g * 16 + col + row * tok_stride;
-  const uint4* vbase = static_cast<const uint4*>(a.v_cache) + g * 16 + col + row * tok_stride;
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
+  // Fused store: this lane's 16 bytes of the new token's K/V row for head g.
+  // They replace what the cache holds at position L-1 when that chunk is
+  // consumed, and are written into the slot then.
+  const int last = r.L - 1;
+  uint4 kn = make_uint4(0, 0, 0, 0), vn = make_uint4(0, 0, 0, 0);
+  if (FUSE) {
+    const int64_t off = (static_cast<int64_t>(b) * a.num_kv_heads + g) * 16 + col;
+    kn = static_cast<const uint4*>(a.k_new)[off];
+    vn = static_cast<const uint4*>(a.v_new)[off];
+  }
 
   float m[G], l[G], acc[G][8];
 #pragma unroll
@@ -158,13 +195,40 @@ decode_partition_kernel(DecodeArgs a) {
   }
 
   // Consume one chunk held in registers (scores, online softmax, P.V).
-  auto consume = [&](const ChunkRegs<NL>& c, int base) {
+  auto consume = [&](ChunkRegs<NL>& c, int base) {
+    if (FUSE && static_cast<unsigned>(last - base) < static_cast<unsigned>(CT)) {
+      // The chunk holding the new token (a wave-uniform test): its lanes take
+      // the new K/V and write them into the slot (head g's 256 bytes; no
+      // workgroup reads that slot from the cache).
+#pragma unroll
+      for (int k = 0; k < NL; ++k) {
+        if (base + 4 * k + row == last) {
+          c.k[k] = kn;
+          c.v[k] = vn;
+          if (c.ok) {
+            const_cast<uint4*>(kbase)[c.off + 4 * k * tok_stride] = kn;
+            const_cast<uint4*>(vbase)[c.off + 4 * k * tok_stride] = vn;
+          }
+        }
+      }
+    }
     float s[NL][G];
     bool valid[NL];
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
       const int t = base + 4 * k + row;
       valid[k] = c.ok && t >= t0 && t < t1;
+#if PK_DECODE_DOT2
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float x = dot2_bf16(c.k[k].x, qp[h].x, 0.f);
+        x = dot2_bf16(c.k[k].y, qp[h].y, x);
+        x = dot2_bf16(c.k[k].z, qp[h].z, x);
+        x = dot2_bf16(c.k[k].w, qp[h].w, x);
+        x = row16_sum(x) * a.scale_log2;
+        s[k][h] = valid[k] ? x : -INFINITY;
+      }
+#else
       float kf[8];
       unpack8(c.k[k], kf);
 #pragma unroll
@@ -175,6 +239,7 @@ decode_partition_kernel(DecodeArgs a) {
         x = row16_sum(x);
         s[k][h] = valid[k] ? x : -INFINITY;
       }
+#endif
     }
     float pw[NL][G];
 #pragma unroll
@@ -215,10 +280,9 @@ decode_partition_kernel(DecodeArgs a) {
   // in-bounds cache hit): a conditional load would make the wait counters
   // assume the worst case at the merge and stall on the prefetch itself.
   const int step = NW * CT;
-  int b0 = (t0 / CT) * CT + wave * CT;
+  int b0 = (t0 / CT) * CT + wave * CT;   // == the speculative chunk when spec
   if (b0 < t1) {
-    ChunkRegs<NL> ca, cb;
-    load_chunk<NL>(ca, a, bt, kbase, vbase, tok_stride, blk_stride, b0);
+    if (!spec) load_chunk<NL>(ca, a, bt, kbase, vbase, tok_stride, blk_stride, b0);
     while (true) {
       const int b1 = b0 + step;
       load_chunk<NL>(cb, a, bt, kbase, vbase, tok_stride, blk_stride, b1 < t1 ? b1 : b0);
@@ -337,12 +401,21 @@ hipError_t launch_group(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
   // Chunks must not straddle a cache block: fall back to 16-token chunks when
   // block_size is not a multiple of the wider chunk.
+  const bool fuse = a.k_new != nullptr;
   if (kDecodeLoads > 4 && a.block_size % (4 * kDecodeLoads) == 0) {
-    hipLaunchKernelGGL((decode_partition_kernel<G, kDecodeWaves, kDecodeLoads>), grid,
-                       dim3(kDecodeWaves * kWave), 0, stream, a);
+    if (fuse)
+      hipLaunchKernelGGL((decode_partition_kernel<G, kDecodeWaves, kDecodeLoads, true>), grid,
+                         dim3(kDecodeWaves * kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_partition_kernel<G, kDecodeWaves, kDecodeLoads, false>), grid,
+                         dim3(kDecodeWaves * kWave), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_partition_kernel<G, kDecodeWaves, 4>), grid,
-                       dim3(kDecodeWaves * kWave), 0, stream, a);
+    if (fuse)
+      hipLaunchKernelGGL((decode_partition_kernel<G, kDecodeWaves, 4, true>), grid,
+                         dim3(kDecodeWaves * kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_partition_kernel<G, kDecodeWaves, 4, false>), grid,
+                         dim3(kDecodeWaves * kWave), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_parts <= 1) return e;

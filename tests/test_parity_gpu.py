@@ -265,3 +265,49 @@ def test_decode_prescaled_q_matches_scaled(gpu_lib):
     y.scale = 1.0
     out2 = run_decode(gpu_lib, to_torch(y, "cuda"), y)
     assert_close(out2, out1.double().cpu().numpy(), max_abs=3e-2, mean_abs=4e-3)
+
+
+# --- fused store + decode -------------------------------------------------------
+
+def _fused_vs_unfused(pk, x, partition_size=0):
+    t1 = to_torch(x, "cuda")
+    pk.kv_store(t1["key"], t1["value"], t1["slot_mapping"], t1["k_cache"], t1["v_cache"])
+    ref = run_decode(pk, t1, x, partition_size=partition_size)
+    t2 = to_torch(x, "cuda")
+    got = pk.paged_decode_store(t2["q"], t2["key"], t2["value"], t2["k_cache"], t2["v_cache"],
+                                t2["block_tables"], t2["context_lens"], x.scale,
+                                sliding_window=x.sliding_window, max_context_len=x.max_context_len,
+                                partition_size=partition_size)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(t1["k_cache"].view(torch.int16), t2["k_cache"].view(torch.int16))
+    assert torch.equal(t1["v_cache"].view(torch.int16), t2["v_cache"].view(torch.int16))
+    return got, t2
+
+
+def test_decode_store_fused_workload(gpu_lib):
+    """16 seqs, ctx U{256..512}: one launch == store then decode, bit for bit,
+    and within the bar of the oracle."""
+    x = W.store_decode()
+    got, _ = _fused_vs_unfused(gpu_lib, x)
+    kc, vc = oracle.kv_store(x.k_cache, x.v_cache, x.key, x.value, x.slot_mapping)
+    assert_close(got, oracle_decode(x, kc, vc))
+
+
+@pytest.mark.parametrize("window,ps", [(0, 0), (0, 64), (0, 256), (17, 0), (256, 64), (1, 0)])
+def test_decode_store_fused_edges(gpu_lib, window, ps):
+    lens = [1, 2, 15, 16, 17, 64, 65, 255, 256, 257, 1000]
+    x = _random_case([39, window, ps], lens, bs=32, window=window)
+    rng = np.random.default_rng([40, window])
+    x.key = W.normal_bf16(rng, (len(lens), 8, 128))
+    x.value = W.normal_bf16(rng, (len(lens), 8, 128))
+    x.slot_mapping = np.array([W.slot_of(x.block_tables, b, L - 1, 32) for b, L in enumerate(lens)],
+                              np.int32)
+    _fused_vs_unfused(gpu_lib, x, partition_size=ps)
+
+
+def test_decode_store_fused_deep_layer(gpu_lib):
+    """A full 64-seq layer of the 28-layer workload, in the bench's launch plan."""
+    x = W.deep_decode_layer(3)
+    got, _ = _fused_vs_unfused(gpu_lib, x)
+    kc, vc = oracle.kv_store(x.k_cache, x.v_cache, x.key, x.value, x.slot_mapping)
+    assert_close(got, oracle_decode(x, kc, vc))
