@@ -324,6 +324,9 @@ pk_status pk_paged_prefill(void* out, const void* q, const void* k_cache, const 
   a.group = num_q_heads / num_kv_heads;
   a.num_blocks = num_blocks;
   a.block_size = block_size;
+  a.block_shift = -1;
+  for (int s = 0; s < 31; ++s)
+    if ((1 << s) == block_size) a.block_shift = s;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.sliding_window = sliding_window;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);

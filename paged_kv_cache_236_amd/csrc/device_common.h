@@ -13,16 +13,19 @@ constexpr int kWave = 64;       // CDNA wavefront width
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float32 -> bf16 bits, round to nearest even.  NaN inputs keep a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// float32 -> bf16, round to nearest even: gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32, two values per instruction).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  bf16x2_t v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Unpack 8 bf16 (one 128-bit load) to float32.
@@ -56,7 +59,6 @@ __device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x,
 
 // a.lo*b.lo + a.hi*b.hi + c for two packed bf16 pairs (fp32 products and sum).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }

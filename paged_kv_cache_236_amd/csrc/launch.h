@@ -63,6 +63,7 @@ struct PrefillArgs {
   int32_t group;
   int32_t num_blocks;
   int32_t block_size;
+  int32_t block_shift;     // log2(block_size) when it is a power of two, else -1
   int32_t max_blocks_per_seq;
   int32_t sliding_window;
   float scale_log2;

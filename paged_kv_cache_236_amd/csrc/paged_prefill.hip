@@ -13,23 +13,41 @@
 // BM = 128 / G query rows, so each K/V tile read from HBM serves every head of
 // the group.  Each wavefront owns 32 columns.
 //
-// Formulation.  Per 64-key tile the wavefront computes S^T = K . Q^T (keys x
+// Formulation.  Per 32-key tile the wavefront computes S^T = K . Q^T (keys x
 // its 32 columns; A = K rows from LDS, B = Q^T held in registers for the whole
 // kernel) and then O^T += V^T . P^T (head dims x columns).  In the 32x32 MFMA
 // output layout a lane holds one column and 16 key rows, which are exactly the
 // key slots the lane must supply as the B operand of the PV product, so the
-// probabilities never leave registers; the online-softmax state (m, l) is
-// per lane.  V is written to LDS transposed (V^T[dim][key]) so that the A
-// operand of PV is two contiguous 8-byte LDS reads per lane.  Both LDS tiles
-// are padded so that the MFMA operand reads are bank-conflict free.
+// probabilities never leave registers; the online-softmax state (m, l) is per
+// lane.  K and V sit in LDS in their natural row layout (one 256-byte row per
+// key); the V^T operand is read with the transposing LDS read
+// (ds_read_b64_tr_b16), which hands each lane four keys of one head dim.
+// 16-byte chunks are XOR-swizzled within a row so that every operand read is
+// bank-conflict free.
 //
-// K/V tiles are fetched through the block table into registers one tile
-// ahead, then written to the other of two LDS buffers: one barrier per tile.
+// Data movement.  K/V tiles (32 keys) go from HBM straight into LDS with the
+// 16-byte global-to-LDS DMA loads (global_load_lds_dwordx4): no registers are
+// spent on staging, and a ring of four LDS stages keeps three tiles in flight
+// while one is consumed.  Each lane picks the global 16-byte chunk that the
+// swizzle places at its LDS position.  The compiler cannot see which LDS bytes
+// a DMA writes and would wait for every pending DMA before any LDS read, so
+// the tile's operand reads are issued as inline assembly and the waits for the
+// ring are explicit (s_waitcnt vmcnt for the wave's own DMAs, then a barrier
+// for everyone's).  Nothing else in the loop touches LDS: block-table entries
+// are read with scalar loads (a 32-key tile spans at most two blocks) and the
+// half-wave exchange uses v_permlane32_swap.
+//
+// Softmax.  Scores are scaled inside the exp argument (one FMA per score), the
+// bf16 probabilities are packed by the hardware converter, and the running max
+// is only raised when a tile's max exceeds it by more than 2^8, so most tiles
+// skip rescaling O (probabilities stay <= 256, far inside fp32 and bf16 range).
 //
 // Work order: query tiles are issued heaviest (latest, most keys) first, and
 // with num_seqs * num_kv_heads a multiple of 8 all tiles of one (b, g) pair land
 // on the same XCD (workgroups are dealt round-robin over the 8 XCDs), so the
 // pair's K/V is reused from that XCD's L2.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -38,150 +56,158 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kBN = 64;                 // keys per tile
-constexpr int kCols = 128;              // query columns (head x row) per workgroup
-constexpr int kThreads = 256;           // 4 wavefronts x 32 columns
-constexpr int kKRow = kHeadDim + 8;     // bf16 per K row in LDS (16-byte pad)
-constexpr int kVRow = kBN + 4;          // bf16 per V^T row in LDS (8-byte pad)
-constexpr int kKTile = kBN * kKRow;     // bf16
-constexpr int kVTile = kHeadDim * kVRow;
+constexpr int kBN = 32;                   // keys per tile
+constexpr int kCols = 128;                // query columns (head x row) per workgroup
+constexpr int kThreads = 256;             // 4 wavefronts x 32 columns
+constexpr int kRow = 256;                 // bytes of one K or V row (128 bf16)
+constexpr int kTile = kBN * kRow;         // bytes of one K or V tile (8 KiB)
+constexpr int kStages = 4;                // LDS ring depth (tiles in flight + 1)
+constexpr int kDmaPerTile = 4;            // DMA instructions per wave per tile (2 K + 2 V)
+constexpr float kRescaleSlack = 8.0f;     // log2 units the running max may lag
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+// ring[stage][0] = K tile, ring[stage][1] = V tile
+__shared__ __attribute__((aligned(1024))) char s_ring[kStages][2][kTile];
 
-// One K/V tile (64 keys) in flight in registers: four 16-byte K chunks and
-// four 16-byte V chunks per thread, plus a validity bit per K chunk's key.
-struct TileRegs {
-  uint4 k0, k1, k2, k3;
-  uint4 v0, v1, v2, v3;
-  uint32_t kvalid;   // bit it: key of K chunk `it` is a valid cache slot
+// Position of 16-byte chunk c (0..15) of key row r in LDS.
+//  K: c ^ (r % 16): the A operand of S^T reads one chunk of rows 0..15 per 16 lanes.
+//  V: c ^ 4 (r % 4): a transposed read covers 4 consecutive rows x 4 chunks per 32 lanes.
+__device__ __forceinline__ int k_pos(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int v_pos(int r, int c) { return c ^ ((r & 3) << 2); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<size_t>(
+      (const __attribute__((address_space(3))) char*)(p)));
+}
+
+// Combine lane l with lane l ^ 32 (v_permlane32_swap hands each lane both
+// values of the pair, in an order that differs between the halves, so only
+// symmetric combinations are taken).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One block-table entry through the scalar cache.  Written out because with
+// LDS DMA in the loop the compiler can no longer prove the table unmodified and
+// would use a vector load, whose use waits for every pending DMA as well.  The
+// table is only read during the kernel.
+__device__ __forceinline__ int32_t table_entry(const int32_t* row, int idx) {
+  int32_t v;
+  const int32_t* p = row + idx;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
+// The (at most two) cache blocks holding keys kb .. kb+31 of the sequence,
+// worked out once per tile in scalar registers.
+struct TileMap {
+  int startA, startB;     // first key of each block
+  int endA;               // first key past block A
+  int64_t baseA, baseB;   // byte offset of each block's row 0, KV head g (slot 0 if bad)
+  bool okA, okB;          // the entries are inside the table and the cache
 };
 
-// Block-table entries of the keys a workgroup touches are staged in LDS once;
-// the host rejects max_blocks_per_seq > kPrefillMaxBlocksPerSeq.
-__shared__ int32_t s_bt[kPrefillMaxBlocksPerSeq];   // entries lb0 .. lb1 of the row
+// How the kernel finds a key's cache block.
+constexpr int kDivBlocks = 0;    // any block size: index by division, a tile may span two blocks
+constexpr int kShiftBlocks = 1;  // power of two below a tile: index by shift, up to two blocks
+constexpr int kTileInBlock = 2;  // power of two >= a tile: every tile lies inside one block
 
-struct Walk {
-  int lb0;
-  int Lk;
-  int block_size;
-  float inv_block_size;
-  int max_blocks;
-  int num_blocks;
-};
-
-// j / block_size for 0 <= j < 2^24 without an integer divide: a float
-// estimate corrected by one step.
-__device__ __forceinline__ int div_bs(int j, const Walk& w) {
-  int q = static_cast<int>(static_cast<float>(j) * w.inv_block_size);
-  q += ((q + 1) * w.block_size <= j) ? 1 : 0;
-  q -= (q * w.block_size > j) ? 1 : 0;
-  return q;
+template <bool POW2>
+__device__ __forceinline__ int div_block(const PrefillArgs& a, int x) {
+  return POW2 ? (x >> a.block_shift) : x / a.block_size;
 }
 
-// Cache slot of key j of the sequence; *valid is false (and the slot 0, a
-// harmless address) when j is past the sequence or its block is outside the
-// table or the cache.  Branch-free.
-__device__ __forceinline__ int64_t key_slot(const Walk& w, int j, bool* valid) {
-  const int lb = div_bs(j, w);
-  bool ok = j < w.Lk && lb < w.max_blocks;
-  const int lbc = ok ? lb : w.lb0;
-  const int blk = s_bt[lbc - w.lb0];
-  ok = ok && static_cast<unsigned>(blk) < static_cast<unsigned>(w.num_blocks);
-  *valid = ok;
-  return ok ? static_cast<int64_t>(blk) * w.block_size + (j - lb * w.block_size) : 0;
+template <bool POW2>
+__device__ __forceinline__ TileMap tile_map(const PrefillArgs& a, const int32_t* bt, int kb, int g,
+                                            int64_t slot_bytes) {
+  TileMap m;
+  const int lbA = div_block<POW2>(a, kb);
+  const int lbB = div_block<POW2>(a, kb + kBN - 1);
+  m.startA = lbA * a.block_size;
+  m.startB = lbB * a.block_size;
+  m.endA = m.startA + a.block_size;
+  const int blkA = table_entry(bt, min(lbA, a.max_blocks_per_seq - 1));
+  const int blkB = lbB == lbA ? blkA : table_entry(bt, min(lbB, a.max_blocks_per_seq - 1));
+  m.okA = lbA < a.max_blocks_per_seq && static_cast<unsigned>(blkA) < static_cast<unsigned>(a.num_blocks);
+  m.okB = lbB < a.max_blocks_per_seq && static_cast<unsigned>(blkB) < static_cast<unsigned>(a.num_blocks);
+  const int64_t head = static_cast<int64_t>(g) * kRow;
+  m.baseA = (m.okA ? static_cast<int64_t>(blkA) * a.block_size * slot_bytes : 0) + head;
+  m.baseB = (m.okB ? static_cast<int64_t>(blkB) * a.block_size * slot_bytes : 0) + head;
+  return m;
 }
 
-// K chunk `it` of thread tid: key (it*256 + tid) / 16, 16-byte column tid % 16;
-// 16 consecutive threads read one 256-byte row.
-__device__ __forceinline__ uint4 load_k_chunk(const PrefillArgs& a, const Walk& w, int kbase,
-                                              int g, int tid, int it, uint32_t& valid) {
-  const int idx = it * kThreads + tid;
-  bool ok;
-  const int64_t s = key_slot(w, kbase + (idx >> 4), &ok);
-  valid |= (ok ? 1u : 0u) << it;
-  const int64_t row_vecs = static_cast<int64_t>(a.num_kv_heads) * 16;
-  return static_cast<const uint4*>(a.k_cache)[s * row_vecs + g * 16 + (idx & 15)];
+// 32-bit mask of the keys kb .. kb+31 that exist and have a valid block.
+__device__ __forceinline__ uint32_t valid_mask(const TileMap& m, int kb, int Lk) {
+  const int n = min(max(Lk - kb, 0), kBN);                 // keys before the end
+  const int na = min(max(m.endA - kb, 0), kBN);            // keys in block A
+  const uint32_t upto_n = n >= kBN ? 0xffffffffu : (1u << n) - 1u;
+  const uint32_t in_a = na >= kBN ? 0xffffffffu : (1u << na) - 1u;
+  return upto_n & ((m.okA ? in_a : 0u) | (m.okB ? ~in_a : 0u));
 }
 
-__device__ __forceinline__ TileRegs load_tile(const PrefillArgs& a, const Walk& w, int kbase,
-                                              int g, int tid) {
-  TileRegs r;
-  r.kvalid = 0;
-  r.k0 = load_k_chunk(a, w, kbase, g, tid, 0, r.kvalid);
-  r.k1 = load_k_chunk(a, w, kbase, g, tid, 1, r.kvalid);
-  r.k2 = load_k_chunk(a, w, kbase, g, tid, 2, r.kvalid);
-  r.k3 = load_k_chunk(a, w, kbase, g, tid, 3, r.kvalid);
-  // V: keys 2p, 2p+1 (p = tid % 32), 16-byte columns tid/32 and tid/32 + 8.
-  // Rows of invalid keys are zeroed: their probability is 0, and a zero row
-  // keeps stale cache contents (possibly NaN patterns) out of P.V.
-  const uint4* vc = static_cast<const uint4*>(a.v_cache);
-  const int64_t row_vecs = static_cast<int64_t>(a.num_kv_heads) * 16;
-  const int p = tid & 31;
-  bool ok0, ok1;
-  const int64_t s0 = key_slot(w, kbase + 2 * p, &ok0);
-  const int64_t s1 = key_slot(w, kbase + 2 * p + 1, &ok1);
-  const uint4* r0 = vc + s0 * row_vecs + g * 16 + (tid >> 5);
-  const uint4* r1 = vc + s1 * row_vecs + g * 16 + (tid >> 5);
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  r.v0 = ok0 ? r0[0] : zero;
-  r.v1 = ok1 ? r1[0] : zero;
-  r.v2 = ok0 ? r0[8] : zero;
-  r.v3 = ok1 ? r1[8] : zero;
-  return r;
+// Zero 16 bytes of LDS.  Written out so the compiler does not wait for the
+// pending global-to-LDS loads (it cannot tell which bytes they write).
+__device__ __forceinline__ void zero_lds16(char* p) {
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  asm volatile("ds_write_b128 %0, %1" ::"v"(lds_addr(p)), "v"(z) : "memory");
 }
 
-__device__ __forceinline__ uint32_t pick_pair(uint32_t a, uint32_t b, int hi) {
-  // (half `hi` of a) | (half `hi` of b) << 16
-  return hi ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+// Eight transposed V^T reads of one PV step: for each m-tile mt, the keys at
+// byte offset OFF (first 8 keys of the step) and OFF + 8 rows (next 8 keys).
+template <int OFF>
+__device__ __forceinline__ void read_vt(u32x2_t (&lo)[4], u32x2_t (&hi)[4], const uint32_t (&addr)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%13"
+      : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]),
+        "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]), "=&v"(hi[3])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "n"(OFF), "n"(OFF + 8 * kRow)
+      : "memory");
 }
 
-// Write the two keys' 8 dims of one 16-byte column into V^T (8 rows, 2 keys each).
-__device__ __forceinline__ void store_vt_pair(uint16_t* vt_lds, int ch, int p, const uint4& a,
-                                              const uint4& b) {
-  uint16_t* base = vt_lds + ch * 8 * kVRow + 2 * p;
-  *reinterpret_cast<uint32_t*>(base + 0 * kVRow) = pick_pair(a.x, b.x, 0);
-  *reinterpret_cast<uint32_t*>(base + 1 * kVRow) = pick_pair(a.x, b.x, 1);
-  *reinterpret_cast<uint32_t*>(base + 2 * kVRow) = pick_pair(a.y, b.y, 0);
-  *reinterpret_cast<uint32_t*>(base + 3 * kVRow) = pick_pair(a.y, b.y, 1);
-  *reinterpret_cast<uint32_t*>(base + 4 * kVRow) = pick_pair(a.z, b.z, 0);
-  *reinterpret_cast<uint32_t*>(base + 5 * kVRow) = pick_pair(a.z, b.z, 1);
-  *reinterpret_cast<uint32_t*>(base + 6 * kVRow) = pick_pair(a.w, b.w, 0);
-  *reinterpret_cast<uint32_t*>(base + 7 * kVRow) = pick_pair(a.w, b.w, 1);
+// Wait until at most N LDS reads are pending; the eight registers of one PV
+// step are in/out operands so none of their uses moves above the wait.
+template <int N>
+__device__ __forceinline__ void wait_vt(u32x2_t (&lo)[4], u32x2_t (&hi)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(lo[0]), "+v"(lo[1]), "+v"(lo[2]), "+v"(lo[3]),
+                 "+v"(hi[0]), "+v"(hi[1]), "+v"(hi[2]), "+v"(hi[3])
+               : "n"(N)
+               : "memory");
 }
 
-__device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* k_lds, uint16_t* vt_lds,
-                                           uint8_t* valid_lds, int tid) {
-  const int key = tid >> 4, ch = tid & 15;
-  *reinterpret_cast<uint4*>(k_lds + (key + 0) * kKRow + ch * 8) = r.k0;
-  *reinterpret_cast<uint4*>(k_lds + (key + 16) * kKRow + ch * 8) = r.k1;
-  *reinterpret_cast<uint4*>(k_lds + (key + 32) * kKRow + ch * 8) = r.k2;
-  *reinterpret_cast<uint4*>(k_lds + (key + 48) * kKRow + ch * 8) = r.k3;
-  if (ch == 0) {
-    valid_lds[key + 0] = r.kvalid & 1u;
-    valid_lds[key + 16] = (r.kvalid >> 1) & 1u;
-    valid_lds[key + 32] = (r.kvalid >> 2) & 1u;
-    valid_lds[key + 48] = (r.kvalid >> 3) & 1u;
-  }
-  const int p = tid & 31;
-  store_vt_pair(vt_lds, tid >> 5, p, r.v0, r.v1);
-  store_vt_pair(vt_lds, (tid >> 5) + 8, p, r.v2, r.v3);
-}
-
-template <int G>
+// POS: the softmax scale is positive, so the max of the raw scores gives the
+// max of the scaled ones and each probability is exp2(fma(s, c, -m)).
+// MODE: block addressing (kDivBlocks, kShiftBlocks or kTileInBlock).
+template <int G, bool POS, int MODE>
 __global__ void __launch_bounds__(kThreads, 2)
 paged_prefill_kernel(PrefillArgs a) {
   constexpr int BM = kCols / G;   // query rows per workgroup
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKTile];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVTile];
-  __shared__ uint8_t s_valid[2][kBN];
+  constexpr bool POW2 = MODE != kDivBlocks;
+  constexpr bool ONE = MODE == kTileInBlock;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hgrp = lane >> 5;   // which 8-element k group of the MFMA operands
   const int c32 = lane & 31;
+  const int i16 = lane & 15;
+  const int half = (lane >> 4) & 1;   // which 16 rows of a 32-row MFMA A operand
   const int hq = a.num_kv_heads * G;
+  const float c = a.scale_log2;
 
   // ---- work item: heaviest query tiles first ------------------------------
   const int npairs = a.num_seqs * a.num_kv_heads;
@@ -201,20 +227,86 @@ paged_prefill_kernel(PrefillArgs a) {
   const int pos_lo = P + qa, pos_hi = P + qb - 1;
   const int kstart = W > 0 ? max(0, pos_lo - W + 1) : 0;
   const int tile0 = kstart / kBN, tile1 = pos_hi / kBN;
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
+  const char* kcache = static_cast<const char*>(a.k_cache);
+  const char* vcache = static_cast<const char*>(a.v_cache);
+  const int64_t slot_bytes = static_cast<int64_t>(a.num_kv_heads) * kRow;
 
-  Walk w;
-  w.Lk = Lk;
-  w.block_size = a.block_size;
-  w.inv_block_size = 1.0f / static_cast<float>(a.block_size);
-  w.max_blocks = a.max_blocks_per_seq;
-  w.num_blocks = a.num_blocks;
-  w.lb0 = min(tile0 * kBN / a.block_size, a.max_blocks_per_seq - 1);
-  {
-    const int lb1 = min((tile1 * kBN + kBN - 1) / a.block_size, a.max_blocks_per_seq - 1);
-    const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
-    for (int i = w.lb0 + tid; i <= lb1; i += kThreads) s_bt[i - w.lb0] = bt[i];
-    __syncthreads();
+  // This lane's two DMA rows of a tile (4 rows per DMA instruction, 2 per wave
+  // for K and 2 for V) and the chunks it fetches for them.
+  int dma_row[2], dma_kchunk[2], dma_vchunk[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    dma_row[j] = 8 * wave + 4 * j + (lane >> 4);
+    dma_kchunk[j] = k_pos(dma_row[j], i16) * 16;
+    dma_vchunk[j] = v_pos(dma_row[j], i16) * 16;
   }
+  // Tile-relative byte offsets of those chunks when the tile lies in one block.
+  uint32_t dma_koff[2], dma_voff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    dma_koff[j] = static_cast<uint32_t>(dma_row[j] * slot_bytes + dma_kchunk[j]);
+    dma_voff[j] = static_cast<uint32_t>(dma_row[j] * slot_bytes + dma_vchunk[j]);
+  }
+  // Last block looked up (tiles inside one block): its logical index, byte
+  // offset of row 0 for KV head g, and whether the entry is valid.
+  int cur_lb = -1;
+  int64_t cur_base = 0;
+  bool cur_ok = false;
+
+  // ---- DMA of one tile into ring stage ST (this wave's 8 K rows and 8 V rows)
+  // Returns whether some row of the tile has a bad block entry (for a tile in
+  // one block: the whole tile, same answer in every wave; otherwise: one of
+  // this wave's rows).  Rows of a bad block read slot 0 of the cache instead.
+  // Spanning tiles read the sequence's last key for keys past its end; a tile
+  // inside one block reads the block's rows past the end (in bounds), and
+  // those V rows are zeroed in LDS before use.
+  auto issue_tile = [&](int kt, auto st) -> bool {
+    constexpr int ST = decltype(st)::value;
+    const int kb = kt * kBN;
+    if constexpr (ONE) {
+      const int lb = kb >> a.block_shift;
+      if (lb != cur_lb) {
+        const int blk = table_entry(bt, min(lb, a.max_blocks_per_seq - 1));
+        cur_ok = lb < a.max_blocks_per_seq && static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
+        cur_base = (cur_ok ? static_cast<int64_t>(blk) * a.block_size * slot_bytes : 0) +
+                   static_cast<int64_t>(g) * kRow;
+        cur_lb = lb;
+      }
+      const int64_t tb = cur_base + static_cast<int64_t>(kb & (a.block_size - 1)) * slot_bytes;
+      const char* ksrc = kcache + tb;
+      const char* vsrc = vcache + tb;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        __builtin_amdgcn_global_load_lds(ksrc + dma_koff[j],
+                                         (__attribute__((address_space(3))) void*)(&s_ring[ST][0][(8 * wave + 4 * j) * kRow]),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vsrc + dma_voff[j],
+                                         (__attribute__((address_space(3))) void*)(&s_ring[ST][1][(8 * wave + 4 * j) * kRow]),
+                                         16, 0, 0);
+      }
+      return !cur_ok;
+    } else {
+      const TileMap m = tile_map<POW2>(a, bt, kb, g, slot_bytes);
+      bool any_bad = false;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int key = kb + dma_row[j];
+        const int kk = min(key, Lk - 1);
+        const bool inA = kk < m.endA;
+        any_bad |= !(inA ? m.okA : m.okB) && key < Lk;
+        const int64_t row = (inA ? m.baseA : m.baseB) +
+                            static_cast<int64_t>(kk - (inA ? m.startA : m.startB)) * slot_bytes;
+        char* kdst = &s_ring[ST][0][(8 * wave + 4 * j) * kRow];
+        char* vdst = &s_ring[ST][1][(8 * wave + 4 * j) * kRow];
+        __builtin_amdgcn_global_load_lds(kcache + row + dma_kchunk[j],
+                                         (__attribute__((address_space(3))) void*)(kdst), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vcache + row + dma_vchunk[j],
+                                         (__attribute__((address_space(3))) void*)(vdst), 16, 0, 0);
+      }
+      return __ballot(any_bad) != 0;
+    }
+  };
 
   // ---- this lane's query column -------------------------------------------
   const int col = wave * 32 + c32;
@@ -223,7 +315,7 @@ paged_prefill_kernel(PrefillArgs a) {
   const bool qvalid = qi < Lq;
   const int qpos = P + qi;
   const int head = g * G + hl;
-  // positions spanned by this wavefront's columns (for skipping masked sub-tiles)
+  // positions spanned by this wavefront's columns (for skipping masked tiles)
   const int wq_lo = qa + (wave * 32) % BM;
   const int wq_hi = min(wq_lo + min(32, BM) - 1, Lq - 1);
   const int wpos_lo = P + wq_lo, wpos_hi = P + wq_hi;
@@ -233,7 +325,28 @@ paged_prefill_kernel(PrefillArgs a) {
     const uint4* qp = static_cast<const uint4*>(a.q) +
                       (static_cast<int64_t>(q0 + (qvalid ? qi : qa)) * hq + head) * 16 + hgrp;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qreg[kk] = as_bf16x8(qp[2 * kk]);
+    for (int kk = 0; kk < 8; ++kk) qreg[kk] = __builtin_bit_cast(bf16x8_t, qp[2 * kk]);
+  }
+
+  // Ring prologue: tiles tile0 .. tile0+2 (clamped to tile1; every DMA is
+  // issued unconditionally so the wait counts below are exact).
+  uint32_t badbits = 0;   // bit s: this wave wrote a row with a bad block entry into stage s
+  badbits |= issue_tile(tile0, std::integral_constant<int, 0>{}) ? 1u : 0u;
+  badbits |= issue_tile(min(tile0 + 1, tile1), std::integral_constant<int, 1>{}) ? 2u : 0u;
+  badbits |= issue_tile(min(tile0 + 2, tile1), std::integral_constant<int, 2>{}) ? 4u : 0u;
+
+  // LDS byte addresses of this lane's operand reads in stage 0 (other stages
+  // are reached through the instructions' immediate offsets).
+  const uint32_t ring0 = lds_addr(&s_ring[0][0][0]);
+  uint32_t kaddr[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) kaddr[kk] = ring0 + c32 * kRow + k_pos(c32, 2 * kk + hgrp) * 16;
+  uint32_t vaddr[4];   // key (4*hgrp + i16/4) of step ks2 = 0, dims of m-tile mt
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int keyA = hgrp * 4 + (i16 >> 2);
+    const int ch = mt * 4 + half * 2 + ((i16 & 3) >> 1);
+    vaddr[mt] = ring0 + kTile + keyA * kRow + v_pos(keyA, ch) * 16 + (i16 & 1) * 8;
   }
 
   f32x16_t o[4];
@@ -243,105 +356,179 @@ paged_prefill_kernel(PrefillArgs a) {
     for (int r = 0; r < 16; ++r) o[mt][r] = 0.f;
   float m = -1.0e30f, lsum = 0.f;
 
-  TileRegs regs = load_tile(a, w, tile0 * kBN, g, tid);
-  store_tile(regs, s_k[0], s_vt[0], s_valid[0], tid);
-  __syncthreads();
-
-  for (int kt = tile0; kt <= tile1; ++kt) {
-    const int buf = (kt - tile0) & 1;
-    const bool more = kt < tile1;
-    if (more) regs = load_tile(a, w, (kt + 1) * kBN, g, tid);
-
+  // One tile: wait for its stage, refill the stage read one step earlier, and
+  // consume it.
+  auto step = [&](int kt, auto st) {
+    constexpr int ST = decltype(st)::value;
+    constexpr int NXT = (ST + kStages - 1) % kStages;
+    constexpr int KOFF = ST * 2 * kTile;          // stage offset of the K tile
+    // This wave's DMAs for the stage are done once at most the two newer
+    // tiles' DMAs are pending; the barrier extends that to every wave (and
+    // tells everyone that stage NXT, refilled next, was fully read).
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 2) * kDmaPerTile) : "memory");
     const int kb = kt * kBN;
-    const uint64_t vmask = __ballot(s_valid[buf][lane] != 0);
-    const bool need_mask = (vmask != ~0ull) || (kb + kBN - 1 > pos_lo) ||
-                           (W > 0 && kb < pos_hi - W + 1);
-    const uint16_t* kl = s_k[buf];
-    const uint16_t* vl = s_vt[buf];
-
-    f32x16_t s[2];
-    bool active[2];
+    const bool bad_tile = (badbits >> ST) & 1u;
+    if constexpr (ONE) {
+      // Zero this wave's V rows without data (all of them for a bad block,
+      // else those past the sequence end) so they cannot reach P.V.
+      if (bad_tile || kb + kBN > Lk) {
+        const int first = bad_tile ? 0 : Lk - kb;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int k0 = kb + sub * 32;
-      active[sub] = k0 <= wpos_hi && k0 < Lk && !(W > 0 && k0 + 31 < wpos_lo - W + 1);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[sub][r] = 0.f;
-      if (active[sub]) {
-        const uint16_t* krow = kl + (sub * 32 + c32) * kKRow + hgrp * 8;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const bf16x8_t kop = as_bf16x8(*reinterpret_cast<const uint4*>(krow + kk * 16));
-          s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[kk], s[sub], 0, 0, 0);
-        }
+        for (int j = 0; j < 2; ++j)
+          if (dma_row[j] >= first) zero_lds16(&s_ring[ST][1][dma_row[j] * kRow + i16 * 16]);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
+    } else if (bad_tile) {
+      // Rare path (a block-table entry outside the cache): zero this wave's V
+      // rows whose key has no valid block, so stale data cannot reach P.V.
+      const uint32_t vm = valid_mask(tile_map<POW2>(a, bt, kb, g, slot_bytes), kb, Lk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (kb + dma_row[j] < Lk && !((vm >> dma_row[j]) & 1u))
+          zero_lds16(&s_ring[ST][1][dma_row[j] * kRow + i16 * 16]);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    __builtin_amdgcn_s_barrier();
+    {
+      const bool bad = issue_tile(min(kt + kStages - 1, tile1), std::integral_constant<int, NXT>{});
+      badbits = (badbits & ~(1u << NXT)) | ((bad ? 1u : 0u) << NXT);
     }
 
-    // online softmax over this lane's column (keys of the tile: 16 per sub-tile
-    // in this lane, the other 16 in lane ^ 32)
-    float mx = -INFINITY;
+    const bool active = kb <= wpos_hi && kb < Lk && !(W > 0 && kb + kBN - 1 < wpos_lo - W + 1);
+    if (!active) return;
+    uint32_t vmask;
+    if constexpr (ONE) {
+      const int n = Lk - kb;   // >= 1: every consumed tile starts before the end
+      vmask = bad_tile ? 0u : (n >= kBN ? 0xffffffffu : (1u << n) - 1u);
+    } else {
+      vmask = valid_mask(tile_map<POW2>(a, bt, kb, g, slot_bytes), kb, Lk);
+    }
+    const bool need_mask = (vmask != 0xffffffffu) || (kb + kBN - 1 > pos_lo) ||
+                           (W > 0 && kb < pos_hi - W + 1);
+
+    // ---- operand reads: K for S^T together with V^T for the first PV step, so
+    // the V latency hides behind the S product and the softmax; the second
+    // step's V^T is read while the first PV step runs.  Each wait takes the
+    // registers it guards as in/out operands, so no use moves above it.
+    u32x4_t kop[8];
+    u32x2_t va[2][4], vbb[2][4];
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%16\n\t"
+        "ds_read_b128 %1, %9 offset:%16\n\t"
+        "ds_read_b128 %2, %10 offset:%16\n\t"
+        "ds_read_b128 %3, %11 offset:%16\n\t"
+        "ds_read_b128 %4, %12 offset:%16\n\t"
+        "ds_read_b128 %5, %13 offset:%16\n\t"
+        "ds_read_b128 %6, %14 offset:%16\n\t"
+        "ds_read_b128 %7, %15 offset:%16"
+        : "=&v"(kop[0]), "=&v"(kop[1]), "=&v"(kop[2]), "=&v"(kop[3]),
+          "=&v"(kop[4]), "=&v"(kop[5]), "=&v"(kop[6]), "=&v"(kop[7])
+        : "v"(kaddr[0]), "v"(kaddr[1]), "v"(kaddr[2]), "v"(kaddr[3]),
+          "v"(kaddr[4]), "v"(kaddr[5]), "v"(kaddr[6]), "v"(kaddr[7]), "n"(KOFF)
+        : "memory");
+    read_vt<KOFF>(va[0], vbb[0], vaddr);
+    // K operands first: the 8 V reads issued after them may still be in flight.
+    asm volatile("s_waitcnt lgkmcnt(8)"
+                 : "+v"(kop[0]), "+v"(kop[1]), "+v"(kop[2]), "+v"(kop[3]),
+                   "+v"(kop[4]), "+v"(kop[5]), "+v"(kop[6]), "+v"(kop[7])
+                 :
+                 : "memory");
+    f32x16_t s;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kop[kk]), qreg[kk],
+                                                  s, 0, 0, 0);
+
+    // ---- online softmax over this lane's column ------------------------------
+    // (16 keys of the tile in this lane, the other 16 in lane ^ 32)
+    float mx = -INFINITY;
+    if (need_mask) {
+      // Keys of the tile this lane's query may see: valid block, causal
+      // (key <= qpos) and inside the window (qpos - key < W), as a bit mask
+      // over the tile's 32 keys, shifted to this lane's key group.
+      const int hi = qpos - kb;                            // last allowed tile key
+      const int lo = W > 0 ? qpos - W + 1 - kb : 0;        // first allowed tile key
+      uint32_t allow = hi < 0 ? 0u : (hi >= 31 ? 0xffffffffu : (2u << hi) - 1u);
+      allow &= lo <= 0 ? 0xffffffffu : (lo > 31 ? 0u : ~((1u << lo) - 1u));
+      allow = ((allow & vmask) >> (hgrp * 4));
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = s[sub][r] * a.scale_log2;
-        if (!active[sub]) {
-          x = -INFINITY;
-        } else if (need_mask) {
-          const int klocal = sub * 32 + (r >> 2) * 8 + hgrp * 4 + (r & 3);
-          const int key = kb + klocal;
-          const bool ok = ((vmask >> klocal) & 1ull) && key <= qpos && (W == 0 || qpos - key < W);
-          x = ok ? x : -INFINITY;
-        }
-        s[sub][r] = x;
-        mx = fmaxf(mx, x);
+        const float x = POS ? s[r] : s[r] * c;
+        s[r] = (allow >> ((r >> 2) * 8 + (r & 3))) & 1u ? x : -INFINITY;
+        mx = fmaxf(mx, s[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (!POS) s[r] *= c;
+        mx = fmaxf(mx, s[r]);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float mn = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - mn);
-    m = mn;
-    lsum *= alpha;
+    mx = max_xor32(mx);
+    const float mcand = POS ? mx * c : mx;   // candidate running max, scaled (log2) units
+    const bool grow = mcand > m + kRescaleSlack;
+    if (__ballot(grow) != 0) {
+      const float mn = grow ? mcand : m;
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      lsum *= alpha;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
-
-    // O^T += V^T . P^T, one 32-key sub-tile at a time.  In step ks2 the lane's
-    // 8 key slots are keys 16*ks2 + 4*hgrp + {0..3} and 16*ks2 + 8 + 4*hgrp +
-    // {0..3} of the sub-tile: accumulator registers 8*ks2 .. 8*ks2+7.
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      if (!active[sub]) continue;
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        uint32_t w[4];
-#pragma unroll
-        for (int r = 0; r < 8; r += 2) {
-          const float p0 = fast_exp2(s[sub][8 * ks2 + r] - mn);
-          const float p1 = fast_exp2(s[sub][8 * ks2 + r + 1] - mn);
-          lsum += p0 + p1;
-          w[r >> 1] = pack_bf16x2(p0, p1);
-        }
-        const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-        const int koff = sub * 32 + ks2 * 16 + hgrp * 4;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const uint16_t* vrow = vl + (mt * 32 + c32) * kVRow + koff;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-          const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, o[mt], 0, 0, 0);
-        }
-      }
+        for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
     }
 
-    if (more) store_tile(regs, s_k[buf ^ 1], s_vt[buf ^ 1], s_valid[buf ^ 1], tid);
-    __syncthreads();
+    // ---- O^T += V^T . P^T ------------------------------------------------------
+    // In step ks2 the lane's 8 key slots are keys 16*ks2 + 4*hgrp + {0..3} and
+    // 16*ks2 + 8 + 4*hgrp + {0..3} of the tile: accumulator registers
+    // 8*ks2 .. 8*ks2+7.  The A operand (V^T: 32 dims x those keys) comes from
+    // two transposed reads; for one of them, lane group i16 supplies the
+    // address of key (base + i16/4), dims (16*half + 4*(i16%4)) .. +4, and
+    // receives dim 16*half + i16 of the four keys.
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      uint32_t pw[4];
+#pragma unroll
+      for (int r = 0; r < 8; r += 2) {
+        const float x0 = s[8 * ks2 + r], x1 = s[8 * ks2 + r + 1];
+        const float p0 = fast_exp2(POS ? fmaf(x0, c, -m) : x0 - m);
+        const float p1 = fast_exp2(POS ? fmaf(x1, c, -m) : x1 - m);
+        lsum += p0 + p1;
+        pw[r >> 1] = pack_bf16x2(p0, p1);
+      }
+      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      if (ks2 == 0) {
+        read_vt<KOFF + 16 * kRow>(va[1], vbb[1], vaddr);
+        wait_vt<8>(va[0], vbb[0]);
+      } else {
+        wait_vt<0>(va[1], vbb[1]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const u32x4_t w = {va[ks2][mt].x, va[ks2][mt].y, vbb[ks2][mt].x, vbb[ks2][mt].y};
+        const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, w);
+        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, o[mt], 0, 0, 0);
+      }
+    }
+  };
+
+  for (int kt = tile0;;) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (++kt > tile1) break;
+    step(kt, std::integral_constant<int, 1>{});
+    if (++kt > tile1) break;
+    step(kt, std::integral_constant<int, 2>{});
+    if (++kt > tile1) break;
+    step(kt, std::integral_constant<int, 3>{});
+    if (++kt > tile1) break;
   }
+  // Drain this wave's remaining (clamped, unused) DMAs before the wave ends.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- normalise and write ---------------------------------------------------
-  const float ltot = lsum + __shfl_xor(lsum, 32, kWave);
+  const float ltot = sum_xor32(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   if (qvalid) {
     uint16_t* orow = static_cast<uint16_t*>(a.out) +
@@ -365,8 +552,19 @@ hipError_t launch_group(const PrefillArgs& a, hipStream_t stream) {
   const int64_t grid = ntiles * a.num_seqs * a.num_kv_heads;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((paged_prefill_kernel<G>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
-                     0, stream, a);
+  const dim3 gr(static_cast<unsigned>(grid)), bl(kThreads);
+  const bool pos = a.scale_log2 > 0.f;
+  const int mode = a.block_shift < 0 ? kDivBlocks : (a.block_size >= kBN ? kTileInBlock : kShiftBlocks);
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, gr, bl, 0, stream, a); };
+  if (pos) {
+    if (mode == kTileInBlock) go(paged_prefill_kernel<G, true, kTileInBlock>);
+    else if (mode == kShiftBlocks) go(paged_prefill_kernel<G, true, kShiftBlocks>);
+    else go(paged_prefill_kernel<G, true, kDivBlocks>);
+  } else {
+    if (mode == kTileInBlock) go(paged_prefill_kernel<G, false, kTileInBlock>);
+    else if (mode == kShiftBlocks) go(paged_prefill_kernel<G, false, kShiftBlocks>);
+    else go(paged_prefill_kernel<G, false, kDivBlocks>);
+  }
   return hipGetLastError();
 }
 
