@@ -34,6 +34,8 @@ pk_status ok() {
 constexpr double kLog2e = 1.4426950408889634;
 constexpr int32_t kHeadDim = 128;
 constexpr int64_t kPartitionQuantum = 64;   // 4 wavefronts x 16-token chunks
+constexpr int64_t kNumCUs = 256;            // MI355X: 8 XCDs x 32 CUs
+constexpr int32_t kOrderMaxSeqs = 64;       // sequences one wavefront can rank
 
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
@@ -96,7 +98,7 @@ pk_status plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max_contex
     // Keys one (sequence, KV head) can attend.
     const int64_t eff = sliding_window > 0 ? std::min<int64_t>(ctx, sliding_window) : ctx;
     const int64_t pairs = static_cast<int64_t>(std::max(num_seqs, 1)) * num_kv_heads;
-    if (pairs >= 256) {
+    if (pairs >= kNumCUs) {
       // The grid already covers every CU: one partition per pair up to 2048
       // keys (no combine launch), 2048-key partitions beyond; a window spans
       // about two partitions of half its size.
@@ -104,9 +106,9 @@ pk_status plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max_contex
       const int64_t want = sliding_window > 0 ? std::max<int64_t>(eff / 2, 64) : std::min<int64_t>(eff, 2048);
       while (ps < want) ps *= 2;
     } else {
-      // Few pairs: split until >= 512 workgroups (2 per CU), 64 keys at least.
+      // Few pairs: split until >= 2 workgroups per CU, 64 keys at least.
       ps = 2048;
-      while (ps > kPartitionQuantum && pairs * slots_for(ctx, sliding_window, ps) < 512) ps /= 2;
+      while (ps > kPartitionQuantum && pairs * slots_for(ctx, sliding_window, ps) < 2 * kNumCUs) ps /= 2;
     }
   }
   const int64_t slots = slots_for(ctx, sliding_window, ps);
@@ -177,6 +179,11 @@ static pk_status paged_decode_impl(void* out, const void* q, const void* k_cache
   a.sliding_window = sliding_window;
   a.partition_size = p.partition_size;
   a.num_parts = p.num_parts;
+  // Length ordering pays when each (seq, KV head) item is one workgroup and
+  // there are more items than CUs (several items share a CU); the in-kernel
+  // ranking handles up to one wavefront of sequences.
+  a.length_order = p.num_parts == 1 && num_seqs <= kOrderMaxSeqs &&
+                   num_seqs * num_kv_heads > kNumCUs;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
   const hipError_t e = pk::launch_paged_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PK_ERR_LAUNCH, "paged_decode launch failed: %s", hipGetErrorString(e));

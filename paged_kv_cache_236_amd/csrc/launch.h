@@ -44,6 +44,7 @@ struct DecodeArgs {
   int32_t sliding_window;
   int32_t partition_size;
   int32_t num_parts;       // partition slots per sequence
+  int32_t length_order;    // 1: workgroups take (seq, head) items longest-first, paired long/short
   float scale_log2;        // softmax scale * log2(e)
 };
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);

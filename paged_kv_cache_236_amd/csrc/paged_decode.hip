@@ -109,6 +109,49 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<NL>& c, const DecodeArgs& a
   for (int k = 0; k < NL; ++k) c.v[k] = load16(vbase + c.off + 4 * k * tok_stride);
 }
 
+// Work order by length.  Workgroups are dealt round-robin over the 8 XCDs and
+// then over each XCD's 32 CUs, so workgroup w (one partition per sequence,
+// grid (1, Hkv, B)) lands on CU slot q = w mod 256 in round r = w / 256.  Items
+// (seq, KV head) are ranked by context length, longest first (all heads of a
+// sequence in a row); round r takes ranks 256r .. 256r+255, in order on even
+// rounds and mirrored on odd ones.  The CUs that got the longest items first
+// get the shortest next, which evens out the bytes each CU streams, and the
+// longest items start first.  Every wavefront ranks the <= 64 context lengths
+// itself (one per lane, ties by index), so no wavefront waits on another.
+__device__ __forceinline__ void length_ordered_item(const DecodeArgs& a, int& b, int& g) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int B = a.num_seqs;
+  const int w = blockIdx.y + a.num_kv_heads * blockIdx.z;
+  const int n = B * a.num_kv_heads;
+  const int r = w / 256, q = w % 256;
+  const int n_r = min(256, n - 256 * r);
+  const int rank = 256 * r + ((r & 1) ? n_r - 1 - q : q);
+  const int target = rank / a.num_kv_heads;   // rank of the sequence
+  g = rank % a.num_kv_heads;
+  const int cap = min(a.max_blocks_per_seq * a.block_size, a.max_context_len);
+  // Unique keys, larger = earlier: length, then lower index first; 0 = no sequence.
+  uint32_t key = 0;
+  if (lane < B) {
+    const int L = min(max(a.context_lens[lane], 0), cap);
+    key = ((static_cast<uint32_t>(L) << 6) | static_cast<uint32_t>(63 - lane)) + 1u;
+  }
+  // Radix select of the key with exactly `target` keys above it, from the top
+  // bit down: among the remaining candidates, those with the bit set are all
+  // above those without, so one ballot per bit decides which group holds it.
+  uint64_t cand = __ballot(lane < B);
+  int need = target;   // candidates above the wanted key not yet skipped
+  const int nbits = 32 - __builtin_clz((static_cast<uint32_t>(cap) << 6) + 64u);
+  for (int bit = nbits - 1; bit >= 0; --bit) {
+    const uint64_t ones = __ballot((key >> bit) & 1u) & cand;
+    const int c = __builtin_popcountll(ones);
+    const bool in_ones = need < c;
+    cand = in_ones ? ones : (cand & ~ones);
+    need = in_ones ? need : need - c;
+  }
+  const uint64_t hit = cand;
+  b = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit)));
+}
+
 template <int G, int NW, int NL, bool FUSE>
 __global__ void __launch_bounds__(NW * kWave)
 decode_partition_kernel(DecodeArgs a) {
@@ -120,8 +163,8 @@ decode_partition_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int row = lane >> 4;   // which of the 4 tokens of a load
   const int col = lane & 15;   // which 16-byte column of the head row
-  const int b = blockIdx.z;
-  const int g = blockIdx.y;
+  int b = blockIdx.z, g = blockIdx.y;
+  if (a.length_order) length_ordered_item(a, b, g);
   const int pi = blockIdx.x;
   const int hq = a.num_kv_heads * G;
 

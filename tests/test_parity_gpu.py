@@ -208,6 +208,29 @@ def test_decode_group_sizes(gpu_lib, hq, hkv):
     assert_close(out, oracle_decode(x))
 
 
+# With at most 64 sequences, one partition each and more (seq, KV head) items
+# than CUs, workgroups take the items in order of context length (ranked inside
+# the kernel): ties, a partial second round of items and empty sequences.
+@pytest.mark.parametrize("case", ["ties", "all_equal", "partial_round", "with_empty"])
+def test_decode_length_ordered_batches(gpu_lib, case):
+    rng = np.random.default_rng([41, len(case)])
+    if case == "ties":
+        lens = rng.choice([1, 17, 300, 300, 1024], size=40).tolist()
+    elif case == "all_equal":
+        lens = [512] * 64
+    elif case == "partial_round":
+        lens = rng.integers(1, 1025, size=33).tolist()      # 264 items for 256 CUs
+    else:
+        lens = rng.choice([0, 0, 5, 700], size=48).tolist()
+    x = _random_case([42, len(case)], lens, bs=256)
+    assert gpu_lib.decode_plan(len(lens), 8, max(lens))[1] == 1
+    out = run_decode(gpu_lib, to_torch(x, "cuda"), x)
+    assert_close(out, oracle_decode(x))
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert not out[b].any()
+
+
 def test_decode_block_permutation_bit_exact(gpu_lib):
     x = _random_case([34], [37, 513, 900, 1024], bs=64)
     out1 = run_decode(gpu_lib, to_torch(x, "cuda"), x, partition_size=256)
@@ -303,6 +326,21 @@ def test_decode_store_fused_edges(gpu_lib, window, ps):
     x.slot_mapping = np.array([W.slot_of(x.block_tables, b, L - 1, 32) for b, L in enumerate(lens)],
                               np.int32)
     _fused_vs_unfused(gpu_lib, x, partition_size=ps)
+
+
+def test_decode_store_fused_length_ordered(gpu_lib):
+    """40 seqs with tied lengths, one partition each: the fused store under the
+    length-ordered work assignment."""
+    lens = np.random.default_rng(43).choice([1, 16, 300, 300, 1024], size=40).tolist()
+    x = _random_case([44], lens, bs=256)
+    rng = np.random.default_rng(45)
+    x.key = W.normal_bf16(rng, (len(lens), 8, 128))
+    x.value = W.normal_bf16(rng, (len(lens), 8, 128))
+    x.slot_mapping = np.array([W.slot_of(x.block_tables, b, L - 1, 256) for b, L in enumerate(lens)],
+                              np.int32)
+    got, _ = _fused_vs_unfused(gpu_lib, x)
+    kc, vc = oracle.kv_store(x.k_cache, x.v_cache, x.key, x.value, x.slot_mapping)
+    assert_close(got, oracle_decode(x, kc, vc))
 
 
 def test_decode_store_fused_deep_layer(gpu_lib):
