@@ -91,18 +91,23 @@ __device__ __forceinline__ uint4 load16(const uint4* p) {
 // 4*NL that divides block_size, so the chunk lies in one cache block).  The
 // table index is clamped into the row, and an entry outside the cache reads
 // block 0 with `ok` false, so every address is in bounds whatever the table
-// holds.
+// holds.  base < 0 asks for a dummy chunk (the prefetch past a wavefront's
+// last chunk, never consumed): it reads the first tokens of cache block 0,
+// which every workgroup shares, so it hits in L2 instead of fetching again
+// from HBM (the K/V loads are non-temporal).
 template <int NL>
 __device__ __forceinline__ void load_chunk(ChunkRegs<NL>& c, const DecodeArgs& a,
                                            const int32_t* bt, const uint4* kbase,
                                            const uint4* vbase, int64_t tok_stride,
                                            int64_t blk_stride, int base) {
-  const int lb = min(base / a.block_size, a.max_blocks_per_seq - 1);
+  const bool dummy = base < 0;
+  const int lb = dummy ? 0 : min(base / a.block_size, a.max_blocks_per_seq - 1);
   int blk = bt[lb];
-  c.ok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
+  c.ok = !dummy && static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
   blk = c.ok ? blk : 0;
-  c.off = static_cast<int64_t>(blk) * blk_stride +
-          static_cast<int64_t>(base - lb * a.block_size) * tok_stride;
+  c.off = dummy ? 0
+                : static_cast<int64_t>(blk) * blk_stride +
+                      static_cast<int64_t>(base - lb * a.block_size) * tok_stride;
 #pragma unroll
   for (int k = 0; k < NL; ++k) c.k[k] = load16(kbase + c.off + 4 * k * tok_stride);
 #pragma unroll
@@ -319,20 +324,20 @@ decode_partition_kernel(DecodeArgs a) {
 
   // Two register buffers in ping-pong: the loads of the next chunk are in
   // flight while the current one is consumed, with no register copies.  The
-  // prefetch is unconditional (past the end it re-reads the current chunk, an
-  // in-bounds cache hit): a conditional load would make the wait counters
-  // assume the worst case at the merge and stall on the prefetch itself.
+  // prefetch is unconditional (past the end it loads the shared dummy chunk):
+  // a conditional load would make the wait counters assume the worst case at
+  // the merge and stall on the prefetch itself.
   const int step = NW * CT;
   int b0 = (t0 / CT) * CT + wave * CT;   // == the speculative chunk when spec
   if (b0 < t1) {
     if (!spec) load_chunk<NL>(ca, a, bt, kbase, vbase, tok_stride, blk_stride, b0);
     while (true) {
       const int b1 = b0 + step;
-      load_chunk<NL>(cb, a, bt, kbase, vbase, tok_stride, blk_stride, b1 < t1 ? b1 : b0);
+      load_chunk<NL>(cb, a, bt, kbase, vbase, tok_stride, blk_stride, b1 < t1 ? b1 : -1);
       consume(ca, b0);
       if (b1 >= t1) break;
       const int b2 = b1 + step;
-      load_chunk<NL>(ca, a, bt, kbase, vbase, tok_stride, blk_stride, b2 < t1 ? b2 : b1);
+      load_chunk<NL>(ca, a, bt, kbase, vbase, tok_stride, blk_stride, b2 < t1 ? b2 : -1);
       consume(cb, b1);
       if (b2 >= t1) break;
       b0 = b2;
