@@ -246,17 +246,13 @@ decode_partition_kernel(DecodeArgs a) {
   auto consume = [&](ChunkRegs<NL>& c, int base) {
     if (FUSE && static_cast<unsigned>(last - base) < static_cast<unsigned>(CT)) {
       // The chunk holding the new token (a wave-uniform test): its lanes take
-      // the new K/V and write them into the slot (head g's 256 bytes; no
-      // workgroup reads that slot from the cache).
+      // the new K/V in place of what the cache holds at that position (the
+      // slot itself is written at the end of the kernel).
 #pragma unroll
       for (int k = 0; k < NL; ++k) {
         if (base + 4 * k + row == last) {
           c.k[k] = kn;
           c.v[k] = vn;
-          if (c.ok) {
-            const_cast<uint4*>(kbase)[c.off + 4 * k * tok_stride] = kn;
-            const_cast<uint4*>(vbase)[c.off + 4 * k * tok_stride] = vn;
-          }
         }
       }
     }
@@ -404,6 +400,20 @@ decode_partition_kernel(DecodeArgs a) {
         a.ws_ml[slot * 2] = mx;
         a.ws_ml[slot * 2 + 1] = ls;
       }
+    }
+  }  if (FUSE && wave == 0 && row == 0 && pi == r.nparts - 1) {
+    // Fused store: head g's 256 bytes of the new K/V go into the slot of
+    // position L-1, once the partition holding it is done.  Stores share the
+    // in-order vector-memory counter with loads, so a store inside the
+    // streaming loop would make every later wait also wait for its write to
+    // be acknowledged; issued last, nothing waits behind it.
+    const int lb = last / a.block_size;   // < max_blocks_per_seq: L is capped
+    const int blk = bt[lb];
+    if (static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks)) {
+      const int64_t off = static_cast<int64_t>(blk) * blk_stride +
+                          static_cast<int64_t>(last - lb * a.block_size) * tok_stride;
+      const_cast<uint4*>(kbase)[off] = kn;
+      const_cast<uint4*>(vbase)[off] = vn;
     }
   }
 }
