@@ -340,6 +340,21 @@ decode_partition_kernel(DecodeArgs a) {
     }
   }
 
+  if (FUSE && wave == 0 && row == 0 && pi == r.nparts - 1) {
+    // Fused store: head g's 256 bytes of the new K/V go into the slot of
+    // position L-1 once wavefront 0 has streamed its chunks.  Stores share
+    // the in-order vector-memory counter with loads, so a store inside the
+    // streaming loop would make every later wait also wait for its write to
+    // be acknowledged; here no load follows, and the merge below hides it.
+    const int lb = last / a.block_size;   // < max_blocks_per_seq: L is capped
+    const int blk = bt[lb];
+    if (static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks)) {
+      const int64_t off = static_cast<int64_t>(blk) * blk_stride +
+                          static_cast<int64_t>(last - lb * a.block_size) * tok_stride;
+      const_cast<uint4*>(kbase)[off] = kn;
+      const_cast<uint4*>(vbase)[off] = vn;
+    }
+  }
   // Merge the 4 rows of the wavefront (lanes l, l^16, l^32, l^48 share a column).
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -401,22 +416,7 @@ decode_partition_kernel(DecodeArgs a) {
         a.ws_ml[slot * 2 + 1] = ls;
       }
     }
-  }  if (FUSE && wave == 0 && row == 0 && pi == r.nparts - 1) {
-    // Fused store: head g's 256 bytes of the new K/V go into the slot of
-    // position L-1, once the partition holding it is done.  Stores share the
-    // in-order vector-memory counter with loads, so a store inside the
-    // streaming loop would make every later wait also wait for its write to
-    // be acknowledged; issued last, nothing waits behind it.
-    const int lb = last / a.block_size;   // < max_blocks_per_seq: L is capped
-    const int blk = bt[lb];
-    if (static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks)) {
-      const int64_t off = static_cast<int64_t>(blk) * blk_stride +
-                          static_cast<int64_t>(last - lb * a.block_size) * tok_stride;
-      const_cast<uint4*>(kbase)[off] = kn;
-      const_cast<uint4*>(vbase)[off] = vn;
-    }
-  }
-}
+  }}
 
 // Merge the partitions of every sequence that has more than one.
 template <int G>
