@@ -71,6 +71,34 @@ def store_bytes(n, hkv, d):
     return n * hkv * d * 2 * 2 * 2 + 4 * n
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_and_prefill.md")
+CSRC = os.path.join(ROOT, "paged_kv_cache_236_amd", "csrc")
+
+
+def profiled_traffic(record: str, kernel_source: str):
+    """HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE counter runs kept
+    in profiles/ (scaled by the copy-kernel calibration: fetch x2, write x1),
+    or None when the kernel's sources changed since the counters were taken."""
+    import hashlib
+    m = hashlib.sha256()
+    for f in (kernel_source, "device_common.h", "launch.h", "api.hip"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            m.update(fh.read())
+    digest = m.hexdigest()[:16]
+    try:
+        with open(TRAFFIC_PROFILE) as fh:
+            lines = fh.read().splitlines()
+    except OSError:
+        return None
+    for line in lines:
+        if not line.startswith("traffic-record:"):
+            continue
+        fields = dict(f.split("=", 1) for f in line.split()[2:])
+        if line.split()[1] == record and fields.get("sources") == digest:
+            return int(round((float(fields["fetch_kib"]) * 2.0 + float(fields["write_kib"])) * 1024))
+    return None
+
+
 def prefill_flops(lq, lk, hq, d, window=0):
     """4*d flops (QK^T and PV) per admitted (query, key) pair per q head."""
     pairs = 0
@@ -235,7 +263,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": (profiled_traffic("decode_c64_fused", "paged_decode.hip")
+                        if not args.unfused else None),
             "bytes_per_launch": launch_bytes,
             "us_per_launch": round(launch_us, 2),
         },
@@ -361,7 +390,7 @@ def prefill_leg(args, pk, W, dev, stream):
         "roofline": {"kernel": "paged_prefill_kernel", "bound": "mfma",
                      "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": profiled_traffic("prefill_prefix", "paged_prefill.hip")},
     }
 
 
