@@ -273,7 +273,9 @@ paged_prefill_kernel(PrefillArgs a) {
                    static_cast<int64_t>(g) * kRow;
         cur_lb = lb;
       }
-      const int64_t tb = cur_base + static_cast<int64_t>(kb & (a.block_size - 1)) * slot_bytes;
+      // (kb mod block_size) * slot_bytes < 2^31: the host picks this mode only then
+      const int64_t tb = cur_base + static_cast<uint32_t>((kb & (a.block_size - 1)) *
+                                                          static_cast<uint32_t>(slot_bytes));
       const char* ksrc = kcache + tb;
       const char* vsrc = vcache + tb;
 #pragma unroll
@@ -319,6 +321,18 @@ paged_prefill_kernel(PrefillArgs a) {
   const int wq_lo = qa + (wave * 32) % BM;
   const int wq_hi = min(wq_lo + min(32, BM) - 1, Lq - 1);
   const int wpos_lo = P + wq_lo, wpos_hi = P + wq_hi;
+  // Per-wavefront tile thresholds (keys kb .. kb+31 of tile kt = kb/32):
+  //  active:    some key is admitted for some row: act_lo <= kt <= act_hi
+  //             (a wavefront without valid rows has act_hi = -1);
+  //  need_mask: some key lies past the earliest row (kt >= diag_tile) or below
+  //             the latest row's window (kt < win_to), or the tile has keys
+  //             without data (past the end: implied by kt >= diag_tile; a bad
+  //             block entry: checked separately).
+  const int last_tile = (Lk - 1) / kBN;
+  const int act_lo = W > 0 ? max(0, wpos_lo - W + 1) / kBN : 0;
+  const int act_hi = wq_lo < Lq ? min(wpos_hi, Lk - 1) / kBN : -1;
+  const int diag_tile = (wpos_lo + 1) / kBN;
+  const int win_to = (W > 0 && wpos_hi - W + 1 > 0) ? (wpos_hi - W + 1 + kBN - 1) / kBN : 0;
 
   bf16x8_t qreg[8];
   {
@@ -330,10 +344,19 @@ paged_prefill_kernel(PrefillArgs a) {
 
   // Ring prologue: tiles tile0 .. tile0+2 (clamped to tile1; every DMA is
   // issued unconditionally so the wait counts below are exact).
-  uint32_t badbits = 0;   // bit s: this wave wrote a row with a bad block entry into stage s
-  badbits |= issue_tile(tile0, std::integral_constant<int, 0>{}) ? 1u : 0u;
-  badbits |= issue_tile(min(tile0 + 1, tile1), std::integral_constant<int, 1>{}) ? 2u : 0u;
-  badbits |= issue_tile(min(tile0 + 2, tile1), std::integral_constant<int, 2>{}) ? 4u : 0u;
+  // Bad block entries: per stage for spanning tiles (bit s: this wave wrote a
+  // row with a bad entry into stage s); for tiles inside one block a sticky
+  // flag (once a bad entry was seen, every later tile looks its block up again).
+  uint32_t badbits = 0;
+  bool bad_seen = false;
+  auto note_bad = [&](bool bad, auto st) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st)::value;
+    if constexpr (ONE) bad_seen |= bad;
+    else badbits = (badbits & ~(1u << ST)) | ((bad ? 1u : 0u) << ST);
+  };
+  note_bad(issue_tile(tile0, std::integral_constant<int, 0>{}), std::integral_constant<int, 0>{});
+  note_bad(issue_tile(min(tile0 + 1, tile1), std::integral_constant<int, 1>{}), std::integral_constant<int, 1>{});
+  note_bad(issue_tile(min(tile0 + 2, tile1), std::integral_constant<int, 2>{}), std::integral_constant<int, 2>{});
 
   // LDS byte addresses of this lane's operand reads in stage 0 (other stages
   // are reached through the instructions' immediate offsets).
@@ -367,18 +390,24 @@ paged_prefill_kernel(PrefillArgs a) {
     // tells everyone that stage NXT, refilled next, was fully read).
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 2) * kDmaPerTile) : "memory");
     const int kb = kt * kBN;
-    const bool bad_tile = (badbits >> ST) & 1u;
+    bool bad_tile = false;
     if constexpr (ONE) {
-      // Zero this wave's V rows without data (all of them for a bad block,
-      // else those past the sequence end) so they cannot reach P.V.
-      if (bad_tile || kb + kBN > Lk) {
+      if (kt == last_tile || bad_seen) {
+        // Zero this wave's V rows without data (all of them for a bad block,
+        // else those past the sequence end) so they cannot reach P.V.
+        if (bad_seen) {
+          const int lb = kb >> a.block_shift;
+          const int blk = table_entry(bt, min(lb, a.max_blocks_per_seq - 1));
+          bad_tile = !(lb < a.max_blocks_per_seq &&
+                       static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks));
+        }
         const int first = bad_tile ? 0 : Lk - kb;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           if (dma_row[j] >= first) zero_lds16(&s_ring[ST][1][dma_row[j] * kRow + i16 * 16]);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
-    } else if (bad_tile) {
+    } else if ((bad_tile = (badbits >> ST) & 1u)) {
       // Rare path (a block-table entry outside the cache): zero this wave's V
       // rows whose key has no valid block, so stale data cannot reach P.V.
       const uint32_t vm = valid_mask(tile_map<POW2>(a, bt, kb, g, slot_bytes), kb, Lk);
@@ -390,21 +419,21 @@ paged_prefill_kernel(PrefillArgs a) {
     }
     __builtin_amdgcn_s_barrier();
     {
-      const bool bad = issue_tile(min(kt + kStages - 1, tile1), std::integral_constant<int, NXT>{});
-      badbits = (badbits & ~(1u << NXT)) | ((bad ? 1u : 0u) << NXT);
+      note_bad(issue_tile(min(kt + kStages - 1, tile1), std::integral_constant<int, NXT>{}),
+               std::integral_constant<int, NXT>{});
     }
 
-    const bool active = kb <= wpos_hi && kb < Lk && !(W > 0 && kb + kBN - 1 < wpos_lo - W + 1);
-    if (!active) return;
-    uint32_t vmask;
+    if (kt < act_lo || kt > act_hi) return;
+    bool need_mask = kt >= diag_tile || kt < win_to;
+    uint32_t vmask = 0xffffffffu;
     if constexpr (ONE) {
-      const int n = Lk - kb;   // >= 1: every consumed tile starts before the end
-      vmask = bad_tile ? 0u : (n >= kBN ? 0xffffffffu : (1u << n) - 1u);
+      if (bad_tile) vmask = 0u;
+      else if (kt == last_tile && Lk - kb < kBN) vmask = (1u << (Lk - kb)) - 1u;
+      need_mask |= bad_tile;
     } else {
       vmask = valid_mask(tile_map<POW2>(a, bt, kb, g, slot_bytes), kb, Lk);
+      need_mask |= vmask != 0xffffffffu;
     }
-    const bool need_mask = (vmask != 0xffffffffu) || (kb + kBN - 1 > pos_lo) ||
-                           (W > 0 && kb < pos_hi - W + 1);
 
     // ---- operand reads: K for S^T together with V^T for the first PV step, so
     // the V latency hides behind the S product and the softmax; the second
@@ -495,8 +524,8 @@ paged_prefill_kernel(PrefillArgs a) {
         const float x0 = s[8 * ks2 + r], x1 = s[8 * ks2 + r + 1];
         const float p0 = fast_exp2(POS ? fmaf(x0, c, -m) : x0 - m);
         const float p1 = fast_exp2(POS ? fmaf(x1, c, -m) : x1 - m);
-        lsum += p0 + p1;
         pw[r >> 1] = pack_bf16x2(p0, p1);
+        lsum = dot2_bf16(pw[r >> 1], 0x3f803f80u, lsum);   // + the two rounded probabilities
       }
       const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
       if (ks2 == 0) {
@@ -554,7 +583,11 @@ hipError_t launch_group(const PrefillArgs& a, hipStream_t stream) {
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 gr(static_cast<unsigned>(grid)), bl(kThreads);
   const bool pos = a.scale_log2 > 0.f;
-  const int mode = a.block_shift < 0 ? kDivBlocks : (a.block_size >= kBN ? kTileInBlock : kShiftBlocks);
+  // Tiles inside one block need a power-of-two block of >= 32 keys and a block
+  // of one KV head's rows under 2 GiB (32-bit offsets inside a block).
+  const bool in_block = a.block_shift >= 0 && a.block_size >= kBN &&
+                        static_cast<int64_t>(a.block_size) * a.num_kv_heads * kRow < (int64_t{1} << 31);
+  const int mode = a.block_shift < 0 ? kDivBlocks : (in_block ? kTileInBlock : kShiftBlocks);
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, gr, bl, 0, stream, a); };
   if (pos) {
     if (mode == kTileInBlock) go(paged_prefill_kernel<G, true, kTileInBlock>);
