@@ -68,8 +68,24 @@ constexpr int kStages = 4;                // LDS ring depth (tiles in flight + 1
 constexpr int kDmaPerTile = 4;            // DMA instructions per wave per tile (2 K + 2 V)
 constexpr float kRescaleSlack = 8.0f;     // log2 units the running max may lag
 
-// ring[stage][0] = K tile, ring[stage][1] = V tile
-__shared__ __attribute__((aligned(1024))) char s_ring[kStages][2][kTile];
+// The ring: one array per stage for K and for V.  Separate arrays let the
+// compiler tell that a read of one stage does not alias a global-to-LDS load
+// into another, so it places the operand reads' waits itself and inserts no
+// wait for the loads in flight into other stages.
+__shared__ __attribute__((aligned(1024))) char s_k0[kTile], s_k1[kTile], s_k2[kTile], s_k3[kTile];
+__shared__ __attribute__((aligned(1024))) char s_v0[kTile], s_v1[kTile], s_v2[kTile], s_v3[kTile];
+
+template <int ST>
+__device__ __forceinline__ char* k_stage() {
+  static_assert(ST >= 0 && ST < kStages, "ring stage");
+  return ST == 0 ? s_k0 : ST == 1 ? s_k1 : ST == 2 ? s_k2 : s_k3;
+}
+template <int ST>
+__device__ __forceinline__ char* v_stage() {
+  static_assert(ST >= 0 && ST < kStages, "ring stage");
+  return ST == 0 ? s_v0 : ST == 1 ? s_v1 : ST == 2 ? s_v2 : s_v3;
+}
+
 
 // Position of 16-byte chunk c (0..15) of key row r in LDS.
 //  K: c ^ (r % 16): the A operand of S^T reads one chunk of rows 0..15 per 16 lanes.
@@ -81,6 +97,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<size_t>(
       (const __attribute__((address_space(3))) char*)(p)));
 }
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8), issued through the builtin so that the compiler's
+// own wait insertion knows which loads they already cover.
+constexpr int waitcnt_vm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+constexpr int waitcnt_lgkm(int n) { return 0xf | (0x3 << 14) | (0x7 << 4) | ((n & 0xf) << 8); }
 
 // Combine lane l with lane l ^ 32 (v_permlane32_swap hands each lane both
 // values of the pair, in an order that differs between the halves, so only
@@ -152,6 +174,24 @@ __device__ __forceinline__ uint32_t valid_mask(const TileMap& m, int kb, int Lk)
   return upto_n & ((m.okA ? in_a : 0u) | (m.okB ? ~in_a : 0u));
 }
 
+// 16-byte global-to-LDS loads (global_load_lds_dwordx4): each lane's 16
+// bytes land at M0 + 16 * lane.  Issued as assembly on purpose: the compiler
+// then does not know that these instructions write LDS, so it inserts no wait
+// for them before the kernel's (compiler-visible) LDS operand reads; the
+// kernel orders them itself (its own wait for its loads, then a barrier).
+// Compiler-generated waits for its own memory loads stay correct: loads
+// complete in order, so unseen older loads only make those waits stricter.
+// `base` is wave-uniform (scalar base + 32-bit lane offset form).
+__device__ __forceinline__ void dma16_saddr(const char* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+// Per-lane 64-bit address form.
+__device__ __forceinline__ void dma16_vaddr(const char* addr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(addr), "s"(lds) : "memory", "m0");
+}
+
 // Zero 16 bytes of LDS.  Written out so the compiler does not wait for the
 // pending global-to-LDS loads (it cannot tell which bytes they write).
 __device__ __forceinline__ void zero_lds16(char* p) {
@@ -159,34 +199,15 @@ __device__ __forceinline__ void zero_lds16(char* p) {
   asm volatile("ds_write_b128 %0, %1" ::"v"(lds_addr(p)), "v"(z) : "memory");
 }
 
-// Eight transposed V^T reads of one PV step: for each m-tile mt, the keys at
-// byte offset OFF (first 8 keys of the step) and OFF + 8 rows (next 8 keys).
-template <int OFF>
-__device__ __forceinline__ void read_vt(u32x2_t (&lo)[4], u32x2_t (&hi)[4], const uint32_t (&addr)[4]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %7, %11 offset:%13"
-      : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]),
-        "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]), "=&v"(hi[3])
-      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "n"(OFF), "n"(OFF + 8 * kRow)
-      : "memory");
-}
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
-// Wait until at most N LDS reads are pending; the eight registers of one PV
-// step are in/out operands so none of their uses moves above the wait.
-template <int N>
-__device__ __forceinline__ void wait_vt(u32x2_t (&lo)[4], u32x2_t (&hi)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(%8)"
-               : "+v"(lo[0]), "+v"(lo[1]), "+v"(lo[2]), "+v"(lo[3]),
-                 "+v"(hi[0]), "+v"(hi[1]), "+v"(hi[2]), "+v"(hi[3])
-               : "n"(N)
-               : "memory");
+// One transposing LDS read (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane i supplies the address of key (base + i/4), dims 4*(i%4)..+3,
+// and receives dim i of the four keys.
+__device__ __forceinline__ u32x2_t read_tr16(const char* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
 }
 
 // POS: the softmax scale is positive, so the max of the raw scores gives the
@@ -280,12 +301,8 @@ paged_prefill_kernel(PrefillArgs a) {
       const char* vsrc = vcache + tb;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        __builtin_amdgcn_global_load_lds(ksrc + dma_koff[j],
-                                         (__attribute__((address_space(3))) void*)(&s_ring[ST][0][(8 * wave + 4 * j) * kRow]),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vsrc + dma_voff[j],
-                                         (__attribute__((address_space(3))) void*)(&s_ring[ST][1][(8 * wave + 4 * j) * kRow]),
-                                         16, 0, 0);
+        dma16_saddr(ksrc, dma_koff[j], lds_addr(&k_stage<ST>()[(8 * wave + 4 * j) * kRow]));
+        dma16_saddr(vsrc, dma_voff[j], lds_addr(&v_stage<ST>()[(8 * wave + 4 * j) * kRow]));
       }
       return !cur_ok;
     } else {
@@ -299,12 +316,8 @@ paged_prefill_kernel(PrefillArgs a) {
         any_bad |= !(inA ? m.okA : m.okB) && key < Lk;
         const int64_t row = (inA ? m.baseA : m.baseB) +
                             static_cast<int64_t>(kk - (inA ? m.startA : m.startB)) * slot_bytes;
-        char* kdst = &s_ring[ST][0][(8 * wave + 4 * j) * kRow];
-        char* vdst = &s_ring[ST][1][(8 * wave + 4 * j) * kRow];
-        __builtin_amdgcn_global_load_lds(kcache + row + dma_kchunk[j],
-                                         (__attribute__((address_space(3))) void*)(kdst), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vcache + row + dma_vchunk[j],
-                                         (__attribute__((address_space(3))) void*)(vdst), 16, 0, 0);
+        dma16_vaddr(kcache + row + dma_kchunk[j], lds_addr(&k_stage<ST>()[(8 * wave + 4 * j) * kRow]));
+        dma16_vaddr(vcache + row + dma_vchunk[j], lds_addr(&v_stage<ST>()[(8 * wave + 4 * j) * kRow]));
       }
       return __ballot(any_bad) != 0;
     }
@@ -334,14 +347,6 @@ paged_prefill_kernel(PrefillArgs a) {
   const int diag_tile = (wpos_lo + 1) / kBN;
   const int win_to = (W > 0 && wpos_hi - W + 1 > 0) ? (wpos_hi - W + 1 + kBN - 1) / kBN : 0;
 
-  bf16x8_t qreg[8];
-  {
-    const uint4* qp = static_cast<const uint4*>(a.q) +
-                      (static_cast<int64_t>(q0 + (qvalid ? qi : qa)) * hq + head) * 16 + hgrp;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qreg[kk] = __builtin_bit_cast(bf16x8_t, qp[2 * kk]);
-  }
-
   // Ring prologue: tiles tile0 .. tile0+2 (clamped to tile1; every DMA is
   // issued unconditionally so the wait counts below are exact).
   // Bad block entries: per stage for spanning tiles (bit s: this wave wrote a
@@ -358,18 +363,32 @@ paged_prefill_kernel(PrefillArgs a) {
   note_bad(issue_tile(min(tile0 + 1, tile1), std::integral_constant<int, 1>{}), std::integral_constant<int, 1>{});
   note_bad(issue_tile(min(tile0 + 2, tile1), std::integral_constant<int, 2>{}), std::integral_constant<int, 2>{});
 
-  // LDS byte addresses of this lane's operand reads in stage 0 (other stages
-  // are reached through the instructions' immediate offsets).
-  const uint32_t ring0 = lds_addr(&s_ring[0][0][0]);
-  uint32_t kaddr[8];
+  // This lane's Q^T operand (kept in registers for the whole kernel), loaded
+  // after the ring prologue's DMAs are on their way.  One wait for everything
+  // then tells the compiler that Q is resident, so it puts no wait for it in
+  // the loop (a compiler wait there would also drain the ring's DMAs, which it
+  // does not see).  Tile0's DMAs were issued with the next two, so waiting
+  // for all three costs about nothing.
+  bf16x8_t qreg[8];
+  {
+    const uint4* qp = static_cast<const uint4*>(a.q) +
+                      (static_cast<int64_t>(q0 + (qvalid ? qi : qa)) * hq + head) * 16 + hgrp;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) kaddr[kk] = ring0 + c32 * kRow + k_pos(c32, 2 * kk + hgrp) * 16;
-  uint32_t vaddr[4];   // key (4*hgrp + i16/4) of step ks2 = 0, dims of m-tile mt
+    for (int kk = 0; kk < 8; ++kk) qreg[kk] = __builtin_bit_cast(bf16x8_t, qp[2 * kk]);
+  }
+
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+  // Byte offsets of this lane's operand reads inside a stage's K and V tiles.
+  int kofs[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) kofs[kk] = c32 * kRow + k_pos(c32, 2 * kk + hgrp) * 16;
+  int vofs[4];   // key (4*hgrp + i16/4) of PV step 0, dims of m-tile mt
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int keyA = hgrp * 4 + (i16 >> 2);
     const int ch = mt * 4 + half * 2 + ((i16 & 3) >> 1);
-    vaddr[mt] = ring0 + kTile + keyA * kRow + v_pos(keyA, ch) * 16 + (i16 & 1) * 8;
+    vofs[mt] = keyA * kRow + v_pos(keyA, ch) * 16 + (i16 & 1) * 8;
   }
 
   f32x16_t o[4];
@@ -384,11 +403,10 @@ paged_prefill_kernel(PrefillArgs a) {
   auto step = [&](int kt, auto st) {
     constexpr int ST = decltype(st)::value;
     constexpr int NXT = (ST + kStages - 1) % kStages;
-    constexpr int KOFF = ST * 2 * kTile;          // stage offset of the K tile
     // This wave's DMAs for the stage are done once at most the two newer
     // tiles' DMAs are pending; the barrier extends that to every wave (and
     // tells everyone that stage NXT, refilled next, was fully read).
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 2) * kDmaPerTile) : "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((kStages - 2) * kDmaPerTile));
     const int kb = kt * kBN;
     bool bad_tile = false;
     if constexpr (ONE) {
@@ -404,8 +422,8 @@ paged_prefill_kernel(PrefillArgs a) {
         const int first = bad_tile ? 0 : Lk - kb;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          if (dma_row[j] >= first) zero_lds16(&s_ring[ST][1][dma_row[j] * kRow + i16 * 16]);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          if (dma_row[j] >= first) zero_lds16(&v_stage<ST>()[dma_row[j] * kRow + i16 * 16]);
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
       }
     } else if ((bad_tile = (badbits >> ST) & 1u)) {
       // Rare path (a block-table entry outside the cache): zero this wave's V
@@ -414,8 +432,8 @@ paged_prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         if (kb + dma_row[j] < Lk && !((vm >> dma_row[j]) & 1u))
-          zero_lds16(&s_ring[ST][1][dma_row[j] * kRow + i16 * 16]);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          zero_lds16(&v_stage<ST>()[dma_row[j] * kRow + i16 * 16]);
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
     }
     __builtin_amdgcn_s_barrier();
     {
@@ -435,33 +453,20 @@ paged_prefill_kernel(PrefillArgs a) {
       need_mask |= vmask != 0xffffffffu;
     }
 
-    // ---- operand reads: K for S^T together with V^T for the first PV step, so
-    // the V latency hides behind the S product and the softmax; the second
-    // step's V^T is read while the first PV step runs.  Each wait takes the
-    // registers it guards as in/out operands, so no use moves above it.
+    // ---- operand reads (compiler-visible: it waits for each just before its
+    // use): K for S^T, then V^T for both PV steps, whose latency hides behind
+    // the S product and the softmax.
     u32x4_t kop[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) kop[kk] = *reinterpret_cast<const u32x4_t*>(k_stage<ST>() + kofs[kk]);
     u32x2_t va[2][4], vbb[2][4];
-    asm volatile(
-        "ds_read_b128 %0, %8 offset:%16\n\t"
-        "ds_read_b128 %1, %9 offset:%16\n\t"
-        "ds_read_b128 %2, %10 offset:%16\n\t"
-        "ds_read_b128 %3, %11 offset:%16\n\t"
-        "ds_read_b128 %4, %12 offset:%16\n\t"
-        "ds_read_b128 %5, %13 offset:%16\n\t"
-        "ds_read_b128 %6, %14 offset:%16\n\t"
-        "ds_read_b128 %7, %15 offset:%16"
-        : "=&v"(kop[0]), "=&v"(kop[1]), "=&v"(kop[2]), "=&v"(kop[3]),
-          "=&v"(kop[4]), "=&v"(kop[5]), "=&v"(kop[6]), "=&v"(kop[7])
-        : "v"(kaddr[0]), "v"(kaddr[1]), "v"(kaddr[2]), "v"(kaddr[3]),
-          "v"(kaddr[4]), "v"(kaddr[5]), "v"(kaddr[6]), "v"(kaddr[7]), "n"(KOFF)
-        : "memory");
-    read_vt<KOFF>(va[0], vbb[0], vaddr);
-    // K operands first: the 8 V reads issued after them may still be in flight.
-    asm volatile("s_waitcnt lgkmcnt(8)"
-                 : "+v"(kop[0]), "+v"(kop[1]), "+v"(kop[2]), "+v"(kop[3]),
-                   "+v"(kop[4]), "+v"(kop[5]), "+v"(kop[6]), "+v"(kop[7])
-                 :
-                 : "memory");
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        va[ks2][mt] = read_tr16(v_stage<ST>() + vofs[mt] + ks2 * 16 * kRow);
+        vbb[ks2][mt] = read_tr16(v_stage<ST>() + vofs[mt] + ks2 * 16 * kRow + 8 * kRow);
+      }
     f32x16_t s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -528,12 +533,6 @@ paged_prefill_kernel(PrefillArgs a) {
         lsum = dot2_bf16(pw[r >> 1], 0x3f803f80u, lsum);   // + the two rounded probabilities
       }
       const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-      if (ks2 == 0) {
-        read_vt<KOFF + 16 * kRow>(va[1], vbb[1], vaddr);
-        wait_vt<8>(va[0], vbb[0]);
-      } else {
-        wait_vt<0>(va[1], vbb[1]);
-      }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const u32x4_t w = {va[ks2][mt].x, va[ks2][mt].y, vbb[ks2][mt].x, vbb[ks2][mt].y};
@@ -554,7 +553,7 @@ paged_prefill_kernel(PrefillArgs a) {
     if (++kt > tile1) break;
   }
   // Drain this wave's remaining (clamped, unused) DMAs before the wave ends.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
   // ---- normalise and write ---------------------------------------------------
   const float ltot = sum_xor32(lsum);
