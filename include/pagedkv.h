@@ -86,7 +86,9 @@ pk_status pk_kv_store(const void* key, const void* value,
 
 /*
  * Decode split planning.  Decode work for one (sequence, KV head) is cut into
- * partitions of `partition_size` tokens (a multiple of 64); each partition is
+ * partitions of `partition_size` tokens (a multiple of 64) starting at its
+ * first admitted key (with a sliding window W: ceil(min(L, W) / partition_size)
+ * partitions); each partition is
  * reduced by one workgroup to a partial softmax state, and a combine kernel
  * merges the partials (split-K / flash-decoding).  When every sequence fits
  * one partition the combine pass is skipped and the partition kernel writes

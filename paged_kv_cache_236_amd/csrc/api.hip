@@ -76,8 +76,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // of W keys starting anywhere inside a partition spans at most
 // (W + PS - 2) / PS + 1 partitions.
 int64_t slots_for(int64_t max_ctx, int64_t window, int64_t ps) {
-  int64_t n = ceil_div(max_ctx, ps);
-  if (window > 0) n = std::min(n, (window + ps - 2) / ps + 1);
+  // Partitions start at each sequence's first admitted key.
+  const int64_t keys = window > 0 ? std::min(max_ctx, window) : max_ctx;
+  const int64_t n = ceil_div(keys, ps);
   return std::max<int64_t>(n, 1);
 }
 
@@ -100,10 +101,9 @@ pk_status plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max_contex
     const int64_t pairs = static_cast<int64_t>(std::max(num_seqs, 1)) * num_kv_heads;
     if (pairs >= kNumCUs) {
       // The grid already covers every CU: one partition per pair up to 2048
-      // keys (no combine launch), 2048-key partitions beyond; a window spans
-      // about two partitions of half its size.
+      // keys (no combine launch), 2048-key partitions beyond.
       ps = 64;
-      const int64_t want = sliding_window > 0 ? std::max<int64_t>(eff / 2, 64) : std::min<int64_t>(eff, 2048);
+      const int64_t want = std::min<int64_t>(eff, 2048);
       while (ps < want) ps *= 2;
     } else {
       // Few pairs: split until >= 2 workgroups per CU, 64 keys at least.

@@ -4,7 +4,7 @@
 // (flash-decoding) with a separate combine kernel.
 //
 // Work decomposition.  For (sequence b, KV head g) the admitted key positions
-// [lo, L) are cut into partitions of PS tokens aligned at multiples of PS.
+// [lo, L) are cut into partitions of PS tokens starting at lo.
 // One workgroup of NW wavefronts reduces one partition; it serves all G query
 // heads that share KV head g, so every K/V byte is read from HBM exactly once.
 //
@@ -52,8 +52,7 @@ constexpr float kEmptyMax = -1.0e30f;   // running max before any key (finite: 2
 struct SeqRange {
   int L;        // admitted keys end (exclusive)
   int lo;       // admitted keys begin
-  int first;    // first partition index touched
-  int nparts;   // partitions touched (0 when L == 0)
+  int nparts;   // partitions of the admitted keys (0 when L == 0)
 };
 
 __device__ __forceinline__ SeqRange seq_range(const DecodeArgs& a, int b) {
@@ -61,8 +60,9 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeArgs& a, int b) {
   const int cap = min(a.max_blocks_per_seq * a.block_size, a.max_context_len);
   r.L = min(max(a.context_lens[b], 0), cap);
   r.lo = a.sliding_window > 0 ? max(0, r.L - a.sliding_window) : 0;
-  r.first = r.lo / a.partition_size;
-  r.nparts = r.L > 0 ? (r.L - 1) / a.partition_size - r.first + 1 : 0;
+  // Partitions start at lo (not at multiples of the partition size), so a
+  // window of W keys takes ceil(W / partition_size) of them.
+  r.nparts = r.L > 0 ? (r.L - r.lo + a.partition_size - 1) / a.partition_size : 0;
   // The host plan sizes num_parts for the worst sequence; the clamp only keeps
   // workspace indexing in bounds should a caller break that contract.
   r.nparts = min(r.nparts, a.num_parts);
@@ -197,9 +197,8 @@ decode_partition_kernel(DecodeArgs a) {
     return;
   }
   if (pi >= r.nparts) return;
-  const int p = r.first + pi;
-  const int t0 = max(p * a.partition_size, r.lo);
-  const int t1 = min((p + 1) * a.partition_size, r.L);
+  const int t0 = r.lo + pi * a.partition_size;
+  const int t1 = min(t0 + a.partition_size, r.L);
 
 #if PK_DECODE_DOT2
   // q kept as packed bf16 pairs; the scale is applied to the reduced score.

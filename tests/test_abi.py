@@ -107,7 +107,9 @@ def test_decode_plan_and_workspace(lib):
     assert lib.pk_paged_decode_plan(64, 8, 8192, 0, 0, ctypes.byref(ps), ctypes.byref(n)) == OK
     assert ps.value % 64 == 0 and n.value == -(-8192 // ps.value)
     assert lib.pk_paged_decode_plan(64, 8, 8192, 256, 256, ctypes.byref(ps), ctypes.byref(n)) == OK
-    assert (ps.value, n.value) == (256, 2)        # a 256-key window spans <= 2 partitions
+    assert (ps.value, n.value) == (256, 1)        # partitions start at the window: one for 256 keys
+    assert lib.pk_paged_decode_plan(64, 8, 8192, 256, 0, ctypes.byref(ps), ctypes.byref(n)) == OK
+    assert (ps.value, n.value) == (256, 1)        # the planner's choice for the long-context window
     assert lib.pk_paged_decode_plan(64, 8, 8192, 1, 64, ctypes.byref(ps), ctypes.byref(n)) == OK
     assert n.value == 1
     ws = lib.pk_paged_decode_workspace_size(64, 16, 8, 128, 8192, 0, 256)
