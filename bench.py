@@ -283,6 +283,7 @@ def main():
         del layers
         result["long_decode"] = long_leg(args, pk, W, dev, stream)
         result["small_decode"] = small_leg(args, pk, W, dev, stream)
+        result["mixed_batch"] = mixed_leg(args, pk, W, dev, stream)
 
     # ---- CPU baseline: the oracle on a bounded sample -------------------------
     if not args.no_cpu_baseline:
@@ -352,6 +353,33 @@ def small_leg(args, pk, W, dev, stream):
                                    "bytes_per_launch": decode_bytes(y.context_lens, 256, 16, 8, 128)
                                    + store_bytes(16, 8, 128)}
     return res
+
+
+def mixed_leg(args, pk, W, dev, stream):
+    """A chunked-prefill step (48 decode sequences + 4 prefill chunks, 3255 query
+    rows, block 256) in one varlen prefill launch."""
+    import numpy as np
+    import torch
+    x = W.mixed_batch()
+    t = W.to_torch(x, dev)
+    lq = np.diff(x.cu_seqlens_q)
+    lk = np.diff(x.cu_seqlens_k)
+    msq = int(lq.max())
+    out = torch.empty_like(t["q"])
+    pk.kv_store(t["key"], t["value"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+
+    def run():
+        pk.paged_prefill(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["cu_seqlens_q"],
+                         t["cu_seqlens_k"], x.scale, max_seqlen_q=msq, out=out)
+    us = time_call(run, stream, 10)
+    flops = prefill_flops(lq, lk, W.NUM_Q_HEADS, W.HEAD_DIM)
+    kv_bytes = int(lk.sum()) * W.NUM_KV_HEADS * W.HEAD_DIM * 2 * 2
+    return {"workload": "chunked-prefill step: 48 decode seqs (ctx U{256..2048}) + 4 prefill chunks "
+                        "(U{256..1024} new over 0-4 blocks), 4096-token budget",
+            "total_q": int(lq.sum()), "us_per_launch": round(us, 2), "flops_per_launch": flops,
+            "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 2),
+            "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "kv_bytes_once": kv_bytes, "kv_GB/s": round(kv_bytes / (us * 1e-6) / 1e9, 1)}
 
 
 def prefill_leg(args, pk, W, dev, stream):

@@ -122,6 +122,25 @@ def test_prefill_single_token_equals_decode(gpu_lib):
     assert_close(dec, ref)
 
 
+def test_mixed_batch_workload(gpu_lib):
+    """A chunked-prefill step in one varlen launch: 48 decode sequences (one
+    new token each) then 4 prefill chunks over cached prefixes, block 256."""
+    x = W.mixed_batch()
+    out, t = run_store_prefill(gpu_lib, x)
+    ref, kc, vc = oracle_prefill(x)
+    assert np.array_equal(bits_of(t["k_cache"]), kc)
+    assert np.array_equal(bits_of(t["v_cache"]), vc)
+    assert_close(out, ref)
+    # The decode rows are one decode step of those sequences.
+    nd = int(np.sum(np.diff(x.cu_seqlens_q) == 1))
+    dec = gpu_lib.paged_decode(t["q"][:nd].contiguous(), t["k_cache"], t["v_cache"],
+                               t["block_tables"][:nd].contiguous(),
+                               torch.from_numpy(x.context_lens[:nd]).cuda(), x.scale,
+                               max_context_len=int(x.context_lens[:nd].max()))
+    assert_close(dec, ref[:nd])
+    assert_close(out[:nd], dec.double().cpu().numpy(), max_abs=2e-2, mean_abs=2e-3)
+
+
 def test_prefill_chunked_matches_whole(gpu_lib):
     """Two chunks (the second one over a prefix that includes the first) give
     the same rows as one pass, within the bf16 bar."""

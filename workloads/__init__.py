@@ -35,6 +35,7 @@ STORE_DECODE = 2        # 16 seqs, ctx U{256..512}, block 256, store new token f
 DEEP_DECODE = 3         # 64 seqs, ctx U{512..1024}, block 256, 28 layers, q pre-scaled
 PREFIX_PREFILL = 4      # 16 seqs, new U{64..512} + prefix of 0-2 full blocks
 LONG_DECODE = 5         # 64 seqs, ctx U{4096..8192}, block 256 (+ window 256 variant)
+MIXED_BATCH = 6         # chunked-prefill step: 48 decode seqs + 4 prefill chunks, block 256
 
 
 def rng_for(workload_id: int, *sub: int) -> np.random.Generator:
@@ -200,6 +201,46 @@ def prefill_inputs(workload_id: int, num_seqs: int, new_lo: int, new_hi: int,
                        cu_seqlens_q=cuq, cu_seqlens_k=cuk)
 
 
+def mixed_inputs(workload_id: int, decode_seqs: int, ctx_lo: int, ctx_hi: int,
+                 prefill_seqs: int, new_lo: int, new_hi: int, prefix_blocks_max: int,
+                 block_size: int, heads=(NUM_Q_HEADS, NUM_KV_HEADS, HEAD_DIM)) -> PagedInputs:
+    """One mixed step of a chunked-prefill scheduler: decode sequences first
+    (one new token each, context L ~ U{ctx_lo..ctx_hi}, i.e. a cached prefix of
+    L - 1), then prefill chunks (new tokens ~ U{new_lo..new_hi} over a cached
+    prefix of 0..prefix_blocks_max full blocks).  The layout is the varlen
+    prefill's: cu_seqlens_q / cu_seqlens_k, new K/V stored through slot_mapping."""
+    hq, hkv, d = heads
+    meta = rng_for(workload_id, 0)
+    dec_ctx = meta.integers(ctx_lo, ctx_hi, endpoint=True, size=decode_seqs)
+    chunk = meta.integers(new_lo, new_hi, endpoint=True, size=prefill_seqs)
+    pref = meta.integers(0, prefix_blocks_max, endpoint=True, size=prefill_seqs) * block_size
+    lq = np.concatenate([np.ones(decode_seqs, np.int64), chunk]).astype(np.int32)
+    lk = np.concatenate([dec_ctx, pref + chunk]).astype(np.int32)
+    n = decode_seqs + prefill_seqs
+    blocks_per_seq = int(max(math.ceil(int(L) / block_size) for L in lk))
+    tables = permuted_block_tables(meta, n, blocks_per_seq)
+    nb = n * blocks_per_seq
+    cuq = np.zeros(n + 1, np.int32)
+    cuq[1:] = np.cumsum(lq)
+    cuk = np.zeros(n + 1, np.int32)
+    cuk[1:] = np.cumsum(lk)
+    total_q = int(cuq[-1])
+    vals = rng_for(workload_id, 1)
+    q = normal_bf16(vals, (total_q, hq, d))
+    kc = normal_bf16(vals, (nb, block_size, hkv, d))
+    vc = normal_bf16(vals, (nb, block_size, hkv, d))
+    key = normal_bf16(vals, (total_q, hkv, d))
+    value = normal_bf16(vals, (total_q, hkv, d))
+    slots = np.concatenate([
+        slot_of(tables, b, np.arange(int(lk[b]) - int(lq[b]), int(lk[b])), block_size) for b in range(n)
+    ]).astype(np.int32)
+    return PagedInputs(q=q, k_cache=kc, v_cache=vc, block_tables=tables,
+                       context_lens=lk, block_size=block_size,
+                       scale=1.0 / math.sqrt(d), sliding_window=0,
+                       key=key, value=value, slot_mapping=slots,
+                       cu_seqlens_q=cuq, cu_seqlens_k=cuk)
+
+
 # --- the five named workloads -------------------------------------------------
 
 def small_decode() -> PagedInputs:
@@ -239,6 +280,18 @@ def long_decode(sliding_window: int = 0, num_seqs: int = 64) -> PagedInputs:
 
 
 LONG_DECODE_BLOCKS = 64 * 32
+
+
+MIXED_BATCH_TOKENS = 4096   # the scheduler's token budget for one step
+
+
+def mixed_batch() -> PagedInputs:
+    """A chunked-prefill step under a 4096-token budget: 48 decode sequences
+    (context U{256..2048}) and 4 prefill chunks (U{256..1024} new tokens over a
+    prefix of 0-4 full blocks), block 256."""
+    x = mixed_inputs(MIXED_BATCH, 48, 256, 2048, 4, 256, 1024, 4, 256)
+    assert int(x.cu_seqlens_q[-1]) <= MIXED_BATCH_TOKENS
+    return x
 
 
 def long_decode_meta(sliding_window: int = 0) -> PagedInputs:
