@@ -212,6 +212,82 @@ pk_status pk_paged_prefill(void* out, const void* q,
                            int32_t num_q_heads, float scale, int32_t sliding_window,
                            void* stream);
 
+/* ------------------------------------------------------------------------
+ * Host-side KV block manager (no GPU work).
+ *
+ * Hands out the cache blocks that the calls above address through
+ * block_tables and slot_mapping, and reuses the full blocks of a prompt whose
+ * K/V were computed before (lunaryes/nano-vllm diagram, "Components" and
+ * "Connections": the scheduler asks a KV block manager for cached blocks;
+ * nano-vllm-sansho README, "Key Features": prefix caching).  The pages fix no
+ * policy; this one is:
+ *  - a full block is identified by a 64-bit chain hash of the previous
+ *    block's hash and its own block_size token ids, and a hit also compares
+ *    its token ids, so a block is shared only when its own tokens are equal
+ *    and the prefix before it has the same chain hash;
+ *  - a new sequence reuses the longest leading run of cached full blocks and
+ *    always computes at least one token (a prompt cached in full recomputes
+ *    its last block into a new block);
+ *  - reference counts track how many sequences hold a block; a block nobody
+ *    holds stays cached until its space is handed out again, least recently
+ *    freed first;
+ *  - only full blocks are shared, so every slot a call writes belongs to one
+ *    sequence.
+ * A hit may name a block that another sequence of the same batch is about to
+ * fill: its K/V are stored (pk_kv_store) before any attention call reads them.
+ * A manager is not thread-safe: one thread (the scheduler) owns it.  Errors
+ * return a non-OK status, set pk_last_error_message(), and leave the manager
+ * unchanged; PK_ERR_WORKSPACE means the free blocks do not suffice.
+ * ---------------------------------------------------------------------- */
+typedef struct pk_block_manager pk_block_manager;
+
+/* A manager of blocks 0 .. num_blocks-1 of block_size slots each, all free.
+ * num_blocks * block_size must fit an int32 slot index.  *out receives the
+ * handle (NULL on error); release it with pk_bm_destroy. */
+pk_status pk_bm_create(int32_t num_blocks, int32_t block_size, pk_block_manager** out);
+void pk_bm_destroy(pk_block_manager* m);
+
+/* Blocks that no sequence holds (cached or empty). */
+pk_status pk_bm_num_free_blocks(const pk_block_manager* m, int32_t* out);
+
+/* How many sequences hold `block`, and whether its content is registered
+ * (findable by prefix hash). */
+pk_status pk_bm_block_info(const pk_block_manager* m, int32_t block, int32_t* ref_count,
+                           int32_t* cached);
+
+/* Admit sequence `seq_id` (unused so far) with its prompt tokens[0..n) (host
+ * memory, n >= 1).  *num_cached_tokens receives how many leading tokens reuse
+ * cached blocks (a multiple of block_size, < n): only tokens from there on
+ * need K/V computed and stored.  The prompt's full blocks become findable by
+ * later calls at once. */
+pk_status pk_bm_allocate(pk_block_manager* m, int64_t seq_id, const int32_t* tokens,
+                         int32_t num_tokens, int32_t* num_cached_tokens);
+
+/* Append one generated token to `seq_id`; takes a new block when the token
+ * opens one and registers a block that it fills. */
+pk_status pk_bm_append(pk_block_manager* m, int64_t seq_id, int32_t token);
+
+/* Drop `seq_id` and its block references (last block first). */
+pk_status pk_bm_free(pk_block_manager* m, int64_t seq_id);
+
+/* Tokens, blocks and cached leading tokens of `seq_id` (NULL outputs skipped). */
+pk_status pk_bm_seq_info(const pk_block_manager* m, int64_t seq_id, int32_t* num_tokens,
+                         int32_t* num_blocks, int32_t* num_cached_tokens);
+
+/* Fill the host arrays one attention call of the sequences seq_ids[0..B)
+ * needs, where the last num_new[b] tokens of sequence b are the new queries
+ * (0 <= num_new[b] <= its length):
+ *   block_tables  [B, max_blocks_per_seq] block ids, rows padded with -1
+ *   cu_seqlens_q  [B + 1] prefix sums of num_new
+ *   cu_seqlens_k  [B + 1] prefix sums of the sequence lengths
+ *   slot_mapping  [cu_seqlens_q[B]] cache slot of each new token, in order
+ *                 (may be NULL when there are no new tokens)
+ * A decode step uses num_new = 1 (context length = cu_seqlens_k difference). */
+pk_status pk_bm_prepare(const pk_block_manager* m, const int64_t* seq_ids, int32_t num_seqs,
+                        const int32_t* num_new, int32_t max_blocks_per_seq,
+                        int32_t* block_tables, int32_t* cu_seqlens_q, int32_t* cu_seqlens_k,
+                        int32_t* slot_mapping);
+
 #ifdef __cplusplus
 }
 #endif

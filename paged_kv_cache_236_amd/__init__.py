@@ -9,11 +9,13 @@ library has not been built, importing this package raises ImportError.
     kv_store(key, value, slot_mapping, k_cache, v_cache)
     paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ...)
     paged_prefill(q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k, scale, ...)
+    BlockManager(num_blocks, block_size)   host-side block allocation with prefix caching
 """
 from __future__ import annotations
 
 import ctypes
 import os
+import weakref
 from typing import Optional
 
 import torch
@@ -21,7 +23,7 @@ import torch
 __all__ = [
     "LIB_PATH", "PagedKVError", "version", "kv_store", "paged_decode", "paged_decode_store",
     "paged_prefill",
-    "decode_plan", "decode_workspace_size",
+    "decode_plan", "decode_workspace_size", "BlockManager",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
@@ -59,6 +61,21 @@ _lib.pk_paged_decode_store.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32,
 _lib.pk_paged_prefill.restype = ctypes.c_int
 _lib.pk_paged_prefill.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p, _p,
                                   _i32, _i32, _i32, _i32, _f32, _i32, _p]
+_i64 = ctypes.c_int64
+_pi32 = ctypes.POINTER(_i32)
+for _name, _args in (
+        ("pk_bm_create", [_i32, _i32, ctypes.POINTER(_p)]),
+        ("pk_bm_num_free_blocks", [_p, _pi32]),
+        ("pk_bm_block_info", [_p, _i32, _pi32, _pi32]),
+        ("pk_bm_allocate", [_p, _i64, _p, _i32, _pi32]),
+        ("pk_bm_append", [_p, _i64, _i32]),
+        ("pk_bm_free", [_p, _i64]),
+        ("pk_bm_seq_info", [_p, _i64, _pi32, _pi32, _pi32]),
+        ("pk_bm_prepare", [_p, _p, _i32, _p, _i32, _p, _p, _p, _p])):
+    getattr(_lib, _name).restype = ctypes.c_int
+    getattr(_lib, _name).argtypes = _args
+_lib.pk_bm_destroy.restype = None
+_lib.pk_bm_destroy.argtypes = [_p]
 
 
 class PagedKVError(RuntimeError):
@@ -257,3 +274,95 @@ def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev),
         nseq, total_q, int(max_seqlen_q), hq, float(scale), sliding_window, _stream(dev)))
     return out
+
+
+def _host_i32(values, name: str) -> torch.Tensor:
+    t = torch.as_tensor(values, dtype=torch.int32, device="cpu").contiguous()
+    if t.dim() != 1:
+        raise ValueError(f"{name} must be one-dimensional")
+    return t
+
+
+class BlockManager:
+    """Host-side KV block manager with prefix caching (pk_bm_* in pagedkv.h).
+
+    Blocks are ids into a cache of ``num_blocks`` blocks of ``block_size``
+    slots.  ``allocate`` admits a sequence and returns how many leading prompt
+    tokens reuse cached blocks; ``append`` adds a generated token; ``free``
+    drops a sequence; ``prepare`` returns the int32 CPU tensors one attention
+    call needs (block_tables, cu_seqlens_q, cu_seqlens_k, slot_mapping).
+    """
+
+    def __init__(self, num_blocks: int, block_size: int):
+        h = _p()
+        _check(_lib.pk_bm_create(int(num_blocks), int(block_size), ctypes.byref(h)))
+        self._h = h
+        self._finalizer = weakref.finalize(self, _lib.pk_bm_destroy, h)
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def close(self) -> None:
+        """Destroy the manager now (otherwise it goes with the object)."""
+        self._finalizer()
+        self._h = _p()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def _handle(self):
+        if not self._h:
+            raise ValueError("BlockManager is closed")
+        return self._h
+
+    @property
+    def num_free_blocks(self) -> int:
+        n = _i32()
+        _check(_lib.pk_bm_num_free_blocks(self._handle(), ctypes.byref(n)))
+        return n.value
+
+    def block_info(self, block: int):
+        """(reference count, whether the block's content is registered)."""
+        ref, cached = _i32(), _i32()
+        _check(_lib.pk_bm_block_info(self._handle(), int(block), ctypes.byref(ref),
+                                     ctypes.byref(cached)))
+        return ref.value, bool(cached.value)
+
+    def allocate(self, seq_id: int, tokens) -> int:
+        t = _host_i32(tokens, "tokens")
+        n = _i32()
+        _check(_lib.pk_bm_allocate(self._handle(), int(seq_id), t.data_ptr(), int(t.numel()),
+                                   ctypes.byref(n)))
+        return n.value
+
+    def append(self, seq_id: int, token: int) -> None:
+        _check(_lib.pk_bm_append(self._handle(), int(seq_id), int(token)))
+
+    def free(self, seq_id: int) -> None:
+        _check(_lib.pk_bm_free(self._handle(), int(seq_id)))
+
+    def seq_info(self, seq_id: int):
+        """(tokens, blocks, cached leading tokens) of a sequence."""
+        a, b, c = _i32(), _i32(), _i32()
+        _check(_lib.pk_bm_seq_info(self._handle(), int(seq_id), ctypes.byref(a), ctypes.byref(b),
+                                   ctypes.byref(c)))
+        return a.value, b.value, c.value
+
+    def prepare(self, seq_ids, num_new, max_blocks_per_seq: int):
+        """block_tables [B, max_blocks_per_seq], cu_seqlens_q [B+1], cu_seqlens_k [B+1]
+        and slot_mapping [sum(num_new)], all int32 CPU tensors."""
+        ids = torch.as_tensor(seq_ids, dtype=torch.int64, device="cpu").contiguous()
+        nn = _host_i32(num_new, "num_new")
+        b = int(ids.numel())
+        if ids.dim() != 1 or nn.numel() != b:
+            raise ValueError("seq_ids and num_new must be one-dimensional and equally long")
+        tables = torch.empty(b, int(max_blocks_per_seq), dtype=torch.int32)
+        cu_q = torch.empty(b + 1, dtype=torch.int32)
+        cu_k = torch.empty(b + 1, dtype=torch.int32)
+        slots = torch.empty(max(int(nn.sum()), 0), dtype=torch.int32)
+        _check(_lib.pk_bm_prepare(self._handle(), ids.data_ptr(), b, nn.data_ptr(),
+                                  int(max_blocks_per_seq), tables.data_ptr(), cu_q.data_ptr(),
+                                  cu_k.data_ptr(), slots.data_ptr()))
+        return tables, cu_q, cu_k, slots

@@ -13,8 +13,18 @@
 #include "pagedkv.h"
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
+
+namespace pk {
+pk_status record_status(pk_status s, const char* message) {
+  if (s == PK_OK) g_last_error.clear();
+  else g_last_error = message;
+  return s;
+}
+}  // namespace pk
+
+namespace {
 
 pk_status fail(pk_status s, const char* fmt, ...) {
   char buf[512];
@@ -22,14 +32,10 @@ pk_status fail(pk_status s, const char* fmt, ...) {
   va_start(ap, fmt);
   std::vsnprintf(buf, sizeof(buf), fmt, ap);
   va_end(ap);
-  g_last_error = buf;
-  return s;
+  return pk::record_status(s, buf);
 }
 
-pk_status ok() {
-  g_last_error.clear();
-  return PK_OK;
-}
+pk_status ok() { return pk::record_status(PK_OK, ""); }
 
 constexpr double kLog2e = 1.4426950408889634;
 constexpr int32_t kHeadDim = 128;
