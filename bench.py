@@ -412,9 +412,23 @@ def prefill_leg(args, pk, W, dev, stream):
     us = e0.elapsed_time(e1) / n * 1e3
     flops = prefill_flops(lq, lk, W.NUM_Q_HEADS, W.HEAD_DIM)
     tflops = flops / (us * 1e-6) / 1e12
+
+    # The step with the new tokens' store: separate kv_store + prefill, and the
+    # fused entry (one launch; it rewrites the same values each time).
+    def unfused():
+        pk.kv_store(t["key"], t["value"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+        run()
+
+    def fused():
+        pk.paged_prefill_store(t["q"], t["key"], t["value"], t["k_cache"], t["v_cache"],
+                               t["block_tables"], t["cu_seqlens_q"], t["cu_seqlens_k"], x.scale,
+                               max_seqlen_q=msq, out=out)
+    us_unfused = time_call(unfused, stream, n)
+    us_fused = time_call(fused, stream, n)
     return {
         "workload": "varlen causal prefill, 16 seqs, new U{64..512}, prefix 0-2 x 256",
         "total_q": int(lq.sum()), "us_per_launch": round(us, 2), "flops_per_launch": flops,
+        "store_then_prefill_us": round(us_unfused, 2), "fused_store_prefill_us": round(us_fused, 2),
         "roofline": {"kernel": "paged_prefill_kernel", "bound": "mfma",
                      "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -212,6 +212,29 @@ pk_status pk_paged_prefill(void* out, const void* q,
                            int32_t num_q_heads, float scale, int32_t sliding_window,
                            void* stream);
 
+/* Prefill with the new tokens' store fused in: the same result as
+ * pk_kv_store of key/value at the slots of positions P_b .. P_b+Lq_b-1 of
+ * each sequence (slot_mapping derived from block_tables) followed by
+ * pk_paged_prefill, bit for bit, in one launch (the pages name kernel fusion
+ * as the lever past graph replay: nano-vllm-sansho README, "Sansho Serving
+ * Roofline Anchors").  The new keys are read from key/value directly.
+ *   key, value  bf16 [total_q, num_kv_heads, head_dim]: row r is the new
+ *               token of query row r (same layout as q's rows)
+ *   k_cache, v_cache  read for the prefix, written at the new positions
+ * A position whose block-table entry lies outside the table or the cache is
+ * not stored (as pk_kv_store skips such a slot).  Queries beyond
+ * max_seqlen_q are neither computed nor stored.  key/value must not alias
+ * the caches or out.  Other arguments and errors as pk_paged_prefill. */
+pk_status pk_paged_prefill_store(void* out, const void* q, const void* key, const void* value,
+                                 void* k_cache, void* v_cache,
+                                 int32_t num_blocks, int32_t block_size,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                                 int32_t num_q_heads, float scale, int32_t sliding_window,
+                                 void* stream);
+
 /* ------------------------------------------------------------------------
  * Host-side KV block manager (no GPU work).
  *

@@ -9,6 +9,7 @@ library has not been built, importing this package raises ImportError.
     kv_store(key, value, slot_mapping, k_cache, v_cache)
     paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ...)
     paged_prefill(q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k, scale, ...)
+    paged_prefill_store(q, key, value, k_cache, v_cache, block_tables, cu_seqlens_q, ...)
     BlockManager(num_blocks, block_size)   host-side block allocation with prefix caching
 """
 from __future__ import annotations
@@ -22,14 +23,14 @@ import torch
 
 __all__ = [
     "LIB_PATH", "PagedKVError", "version", "kv_store", "paged_decode", "paged_decode_store",
-    "paged_prefill",
+    "paged_prefill", "paged_prefill_store",
     "decode_plan", "decode_workspace_size", "BlockManager",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_236_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python paged_kv_cache_236_amd/build.py` "
         "(or __graft_entry__.build()); there is no non-HIP implementation")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -61,6 +62,9 @@ _lib.pk_paged_decode_store.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32,
 _lib.pk_paged_prefill.restype = ctypes.c_int
 _lib.pk_paged_prefill.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p, _p,
                                   _i32, _i32, _i32, _i32, _f32, _i32, _p]
+_lib.pk_paged_prefill_store.restype = ctypes.c_int
+_lib.pk_paged_prefill_store.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32,
+                                        _p, _p, _i32, _i32, _i32, _i32, _f32, _i32, _p]
 _i64 = ctypes.c_int64
 _pi32 = ctypes.POINTER(_i32)
 for _name, _args in (
@@ -267,6 +271,42 @@ def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         raise ValueError("out must have q's shape")
     _check(_lib.pk_paged_prefill(
         _dev(out, "out", torch.bfloat16, dev), _dev(q, "q", torch.bfloat16, dev),
+        _dev(k_cache, "k_cache", torch.bfloat16, dev), _dev(v_cache, "v_cache", torch.bfloat16, dev),
+        nb, bs, hkv, d,
+        _dev(block_tables, "block_tables", torch.int32, dev), int(block_tables.shape[1]),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev),
+        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev),
+        nseq, total_q, int(max_seqlen_q), hq, float(scale), sliding_window, _stream(dev)))
+    return out
+
+
+def paged_prefill_store(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                        k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                        cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, scale: float, *,
+                        max_seqlen_q: int, sliding_window: int = 0,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Store the new tokens key/value [total_q, num_kv_heads, 128] at their
+    positions (from block_tables) and run the varlen prefill, in one launch."""
+    nb, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    dev = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [total_q, num_q_heads, head_dim]")
+    total_q, hq, qd = (int(x) for x in q.shape)
+    if qd != d:
+        raise ValueError("q and cache head_dim differ")
+    if key.shape != (total_q, hkv, d) or value.shape != (total_q, hkv, d):
+        raise ValueError(f"key/value must be [{total_q}, {hkv}, {d}]")
+    nseq = int(cu_seqlens_q.numel()) - 1
+    if nseq < 0 or cu_seqlens_k.shape != cu_seqlens_q.shape or block_tables.dim() != 2 \
+            or block_tables.shape[0] != nseq:
+        raise ValueError("cu_seqlens_q/k must be [num_seqs+1] and block_tables [num_seqs, max_blocks]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _check(_lib.pk_paged_prefill_store(
+        _dev(out, "out", torch.bfloat16, dev), _dev(q, "q", torch.bfloat16, dev),
+        _dev(key, "key", torch.bfloat16, dev), _dev(value, "value", torch.bfloat16, dev),
         _dev(k_cache, "k_cache", torch.bfloat16, dev), _dev(v_cache, "v_cache", torch.bfloat16, dev),
         nb, bs, hkv, d,
         _dev(block_tables, "block_tables", torch.int32, dev), int(block_tables.shape[1]),

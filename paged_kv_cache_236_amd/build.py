@@ -1,6 +1,6 @@
 """Build step: compile the HIP sources under csrc/ into libpagedkv.so (gfx950).
 
-Run as ``python -m paged_kv_cache_236_amd.build`` or through
+Run as ``python paged_kv_cache_236_amd/build.py`` or through
 ``__graft_entry__.build()``.  The library is built in-tree, next to this file.
 """
 from __future__ import annotations

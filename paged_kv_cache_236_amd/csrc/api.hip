@@ -299,13 +299,16 @@ pk_status pk_paged_decode_store(void* out, const void* q, const void* k_new, con
                            workspace, workspace_bytes, stream, k_new, v_new);
 }
 
-pk_status pk_paged_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
-                           int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
-                           int32_t head_dim, const int32_t* block_tables,
-                           int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
-                           const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t total_q,
-                           int32_t max_seqlen_q, int32_t num_q_heads, float scale,
-                           int32_t sliding_window, void* stream) {
+namespace {
+
+pk_status prefill_common(void* out, const void* q, const void* k_new, const void* v_new,
+                         const void* k_cache, const void* v_cache, int32_t num_blocks,
+                         int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                         int32_t num_q_heads, float scale, int32_t sliding_window, bool fused,
+                         void* stream) {
   pk_status s = check_cache_shape(num_blocks, block_size, num_kv_heads, head_dim);
   if (s != PK_OK) return s;
   if ((s = check_heads(num_q_heads, num_kv_heads)) != PK_OK) return s;
@@ -322,11 +325,14 @@ pk_status pk_paged_prefill(void* out, const void* q, const void* k_cache, const 
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !cu_seqlens_k)
     return fail(PK_ERR_INVALID_ARG, "null pointer argument");
+  if (fused && (!k_new || !v_new)) return fail(PK_ERR_INVALID_ARG, "null key or value");
   pk::PrefillArgs a;
   a.out = out;
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
+  a.k_new = fused ? k_new : nullptr;
+  a.v_new = fused ? v_new : nullptr;
   a.block_tables = block_tables;
   a.cu_seqlens_q = cu_seqlens_q;
   a.cu_seqlens_k = cu_seqlens_k;
@@ -348,6 +354,35 @@ pk_status pk_paged_prefill(void* out, const void* q, const void* k_cache, const 
     return fail(PK_ERR_UNSUPPORTED, "paged_prefill: this configuration is not implemented");
   if (e != hipSuccess) return fail(PK_ERR_LAUNCH, "paged_prefill launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+pk_status pk_paged_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                           int32_t head_dim, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t total_q,
+                           int32_t max_seqlen_q, int32_t num_q_heads, float scale,
+                           int32_t sliding_window, void* stream) {
+  return prefill_common(out, q, nullptr, nullptr, k_cache, v_cache, num_blocks, block_size,
+                        num_kv_heads, head_dim, block_tables, max_blocks_per_seq, cu_seqlens_q,
+                        cu_seqlens_k, num_seqs, total_q, max_seqlen_q, num_q_heads, scale,
+                        sliding_window, false, stream);
+}
+
+pk_status pk_paged_prefill_store(void* out, const void* q, const void* key, const void* value,
+                                 void* k_cache, void* v_cache, int32_t num_blocks,
+                                 int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                                 int32_t num_q_heads, float scale, int32_t sliding_window,
+                                 void* stream) {
+  return prefill_common(out, q, key, value, k_cache, v_cache, num_blocks, block_size,
+                        num_kv_heads, head_dim, block_tables, max_blocks_per_seq, cu_seqlens_q,
+                        cu_seqlens_k, num_seqs, total_q, max_seqlen_q, num_q_heads, scale,
+                        sliding_window, true, stream);
 }
 
 }  // extern "C"

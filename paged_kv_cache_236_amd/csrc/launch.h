@@ -52,8 +52,10 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 struct PrefillArgs {
   void* out;
   const void* q;
-  const void* k_cache;
+  const void* k_cache;         // written too when k_new is set
   const void* v_cache;
+  const void* k_new;           // bf16 [total_q, num_kv_heads, 128]: the new tokens' K/V, stored
+  const void* v_new;           // by the kernel and read from here; nullptr: already in the cache
   const int32_t* block_tables;
   const int32_t* cu_seqlens_q;
   const int32_t* cu_seqlens_k;

@@ -29,13 +29,20 @@
 // 16-byte global-to-LDS DMA loads (global_load_lds_dwordx4): no registers are
 // spent on staging, and a ring of four LDS stages keeps three tiles in flight
 // while one is consumed.  Each lane picks the global 16-byte chunk that the
-// swizzle places at its LDS position.  The compiler cannot see which LDS bytes
-// a DMA writes and would wait for every pending DMA before any LDS read, so
-// the tile's operand reads are issued as inline assembly and the waits for the
-// ring are explicit (s_waitcnt vmcnt for the wave's own DMAs, then a barrier
-// for everyone's).  Nothing else in the loop touches LDS: block-table entries
-// are read with scalar loads (a 32-key tile spans at most two blocks) and the
-// half-wave exchange uses v_permlane32_swap.
+// swizzle places at its LDS position.  The DMA is issued as inline assembly,
+// so the compiler does not see it and does not drain every pending DMA before
+// each (compiler-visible) operand read; the waits for the ring are explicit
+// (s_waitcnt vmcnt for the wave's own DMAs, then a barrier for everyone's).
+// Nothing else in the loop touches LDS: block-table entries are read with
+// scalar loads (a 32-key tile spans at most two blocks) and the half-wave
+// exchange uses v_permlane32_swap.
+//
+// Fused store (FUSE): the new tokens' K/V arrive as separate arrays; tiles
+// read keys at positions >= P_b from those arrays instead of the cache, and
+// each workgroup writes the rows of its own query positions into their cache
+// slots at the end.  Key validity (a bad block-table entry) is decided from
+// the table exactly as without fusion, so the result and the cache equal a
+// store followed by the plain kernel, bit for bit.
 //
 // Softmax.  Scores are scaled inside the exp argument (one FMA per score), the
 // bf16 probabilities are packed by the hardware converter, and the running max
@@ -186,6 +193,15 @@ __device__ __forceinline__ void dma16_saddr(const char* base, uint32_t voff, uin
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
+// A wave-uniform pointer as a scalar value (both 32-bit halves read from the
+// first lane; each half widened as unsigned so the low word is not sign
+// extended).
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(v))));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(v >> 32))));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 // Per-lane 64-bit address form.
 __device__ __forceinline__ void dma16_vaddr(const char* addr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
@@ -213,7 +229,8 @@ __device__ __forceinline__ u32x2_t read_tr16(const char* p) {
 // POS: the softmax scale is positive, so the max of the raw scores gives the
 // max of the scaled ones and each probability is exp2(fma(s, c, -m)).
 // MODE: block addressing (kDivBlocks, kShiftBlocks or kTileInBlock).
-template <int G, bool POS, int MODE>
+// FUSE: store the new tokens (a.k_new / a.v_new) and read them from there.
+template <int G, bool POS, int MODE, bool FUSE>
 __global__ void __launch_bounds__(kThreads, 2)
 paged_prefill_kernel(PrefillArgs a) {
   constexpr int BM = kCols / G;   // query rows per workgroup
@@ -252,6 +269,11 @@ paged_prefill_kernel(PrefillArgs a) {
   const char* kcache = static_cast<const char*>(a.k_cache);
   const char* vcache = static_cast<const char*>(a.v_cache);
   const int64_t slot_bytes = static_cast<int64_t>(a.num_kv_heads) * kRow;
+  // New key j >= P lives in row q0 + j - P of the new-token arrays (the same
+  // row stride as the cache), KV head g.
+  const int64_t new_base = (static_cast<int64_t>(q0) - P) * slot_bytes + static_cast<int64_t>(g) * kRow;
+  const char* knew = FUSE ? static_cast<const char*>(a.k_new) + new_base : nullptr;
+  const char* vnew = FUSE ? static_cast<const char*>(a.v_new) + new_base : nullptr;
 
   // This lane's two DMA rows of a tile (4 rows per DMA instruction, 2 per wave
   // for K and 2 for V) and the chunks it fetches for them.
@@ -297,8 +319,34 @@ paged_prefill_kernel(PrefillArgs a) {
       // (kb mod block_size) * slot_bytes < 2^31: the host picks this mode only then
       const int64_t tb = cur_base + static_cast<uint32_t>((kb & (a.block_size - 1)) *
                                                           static_cast<uint32_t>(slot_bytes));
-      const char* ksrc = kcache + tb;
-      const char* vsrc = vcache + tb;
+      if (FUSE && kb >= P && kb + kBN <= Lk) {
+        // All 32 keys new: consecutive rows of the new-token arrays, with the
+        // cache's row stride, so the same lane offsets apply.
+        const char* ks = uniform_ptr(knew + static_cast<int64_t>(kb) * slot_bytes);
+        const char* vs = uniform_ptr(vnew + static_cast<int64_t>(kb) * slot_bytes);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          dma16_saddr(ks, dma_koff[j], lds_addr(&k_stage<ST>()[(8 * wave + 4 * j) * kRow]));
+          dma16_saddr(vs, dma_voff[j], lds_addr(&v_stage<ST>()[(8 * wave + 4 * j) * kRow]));
+        }
+        return !cur_ok;
+      }
+      if (FUSE && kb + kBN > P) {
+        // Keys >= P from the new-token arrays (past the end: the last key),
+        // earlier ones from the cache block.
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int key = min(kb + dma_row[j], Lk - 1);
+          const int64_t crow = tb + static_cast<int64_t>(dma_row[j]) * slot_bytes;
+          const char* ks = key >= P ? knew + static_cast<int64_t>(key) * slot_bytes : kcache + crow;
+          const char* vs = key >= P ? vnew + static_cast<int64_t>(key) * slot_bytes : vcache + crow;
+          dma16_vaddr(ks + dma_kchunk[j], lds_addr(&k_stage<ST>()[(8 * wave + 4 * j) * kRow]));
+          dma16_vaddr(vs + dma_vchunk[j], lds_addr(&v_stage<ST>()[(8 * wave + 4 * j) * kRow]));
+        }
+        return !cur_ok;
+      }
+      const char* ksrc = uniform_ptr(kcache + tb);
+      const char* vsrc = uniform_ptr(vcache + tb);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         dma16_saddr(ksrc, dma_koff[j], lds_addr(&k_stage<ST>()[(8 * wave + 4 * j) * kRow]));
@@ -316,8 +364,11 @@ paged_prefill_kernel(PrefillArgs a) {
         any_bad |= !(inA ? m.okA : m.okB) && key < Lk;
         const int64_t row = (inA ? m.baseA : m.baseB) +
                             static_cast<int64_t>(kk - (inA ? m.startA : m.startB)) * slot_bytes;
-        dma16_vaddr(kcache + row + dma_kchunk[j], lds_addr(&k_stage<ST>()[(8 * wave + 4 * j) * kRow]));
-        dma16_vaddr(vcache + row + dma_vchunk[j], lds_addr(&v_stage<ST>()[(8 * wave + 4 * j) * kRow]));
+        const bool fresh = FUSE && kk >= P;
+        const char* ks = fresh ? knew + static_cast<int64_t>(kk) * slot_bytes : kcache + row;
+        const char* vs = fresh ? vnew + static_cast<int64_t>(kk) * slot_bytes : vcache + row;
+        dma16_vaddr(ks + dma_kchunk[j], lds_addr(&k_stage<ST>()[(8 * wave + 4 * j) * kRow]));
+        dma16_vaddr(vs + dma_vchunk[j], lds_addr(&v_stage<ST>()[(8 * wave + 4 * j) * kRow]));
       }
       return __ballot(any_bad) != 0;
     }
@@ -555,6 +606,56 @@ paged_prefill_kernel(PrefillArgs a) {
   // Drain this wave's remaining (clamped, unused) DMAs before the wave ends.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
+  // ---- fused store: this workgroup's new tokens into their cache slots -------
+  // Rows P+qa .. P+qb-1 of KV head g, 16 lanes per 256-byte row, four rows per
+  // thread per round.  The first round's rows and block-table entries are
+  // loaded here and stored after the output rows are written, so the loads'
+  // latency overlaps that write; more rounds (one query head per KV head)
+  // follow.  Done last: a store inside or before the loop would hold up the
+  // loop's DMA waits (stores and loads share the in-order vector-memory
+  // counter) until its write is acknowledged.  A position whose block-table
+  // entry is outside the table or the cache is not stored.
+  const int st_rows = qb - qa;
+  const int64_t st_src0 = (static_cast<int64_t>(q0) + qa) * slot_bytes + static_cast<int64_t>(g) * kRow +
+                          (tid & 15) * 16;
+  constexpr int kStride = kThreads / 16;   // rows covered by one pass of the workgroup
+  struct StoreRound {
+    int r[4], lb[4], blk[4];
+    uint4 k[4], v[4];
+  };
+  auto st_load = [&](StoreRound& R, int r0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      R.r[i] = r0 + i * kStride;
+      const int rr = min(R.r[i], st_rows - 1);
+      R.lb[i] = div_block<POW2>(a, P + qa + rr);
+      R.blk[i] = bt[min(R.lb[i], a.max_blocks_per_seq - 1)];   // read in bounds, judged at the store
+      R.k[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + st_src0 +
+                                               static_cast<int64_t>(rr) * slot_bytes);
+      R.v[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + st_src0 +
+                                               static_cast<int64_t>(rr) * slot_bytes);
+    }
+    // Keep the table reads unconditional, so all twelve loads are in flight together.
+    asm volatile("" : "+v"(R.blk[0]), "+v"(R.blk[1]), "+v"(R.blk[2]), "+v"(R.blk[3]));
+  };
+  auto st_store = [&](const StoreRound& R) __attribute__((always_inline)) {
+    char* kdst = static_cast<char*>(const_cast<void*>(a.k_cache)) + static_cast<int64_t>(g) * kRow + (tid & 15) * 16;
+    char* vdst = static_cast<char*>(const_cast<void*>(a.v_cache)) + static_cast<int64_t>(g) * kRow + (tid & 15) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = R.r[i] < st_rows && R.lb[i] < a.max_blocks_per_seq &&
+                      static_cast<unsigned>(R.blk[i]) < static_cast<unsigned>(a.num_blocks);
+      if (ok) {
+        const int pos = P + qa + R.r[i];
+        const int64_t dst = (static_cast<int64_t>(R.blk[i]) * a.block_size + pos % a.block_size) * slot_bytes;
+        *reinterpret_cast<uint4*>(kdst + dst) = R.k[i];
+        *reinterpret_cast<uint4*>(vdst + dst) = R.v[i];
+      }
+    }
+  };
+  StoreRound st_first;
+  if constexpr (FUSE) st_load(st_first, tid >> 4);
+
   // ---- normalise and write ---------------------------------------------------
   const float ltot = sum_xor32(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
@@ -570,6 +671,15 @@ paged_prefill_kernel(PrefillArgs a) {
                                    pack_bf16x2(o[mt][rg * 4 + 2] * inv, o[mt][rg * 4 + 3] * inv));
         *reinterpret_cast<uint2*>(orow + dim) = v;
       }
+  }
+
+  if constexpr (FUSE) {
+    st_store(st_first);
+    for (int r0 = (tid >> 4) + 4 * kStride; r0 < st_rows; r0 += 4 * kStride) {
+      StoreRound R;
+      st_load(R, r0);
+      st_store(R);
+    }
   }
 }
 
@@ -588,15 +698,20 @@ hipError_t launch_group(const PrefillArgs& a, hipStream_t stream) {
                         static_cast<int64_t>(a.block_size) * a.num_kv_heads * kRow < (int64_t{1} << 31);
   const int mode = a.block_shift < 0 ? kDivBlocks : (in_block ? kTileInBlock : kShiftBlocks);
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, gr, bl, 0, stream, a); };
-  if (pos) {
-    if (mode == kTileInBlock) go(paged_prefill_kernel<G, true, kTileInBlock>);
-    else if (mode == kShiftBlocks) go(paged_prefill_kernel<G, true, kShiftBlocks>);
-    else go(paged_prefill_kernel<G, true, kDivBlocks>);
-  } else {
-    if (mode == kTileInBlock) go(paged_prefill_kernel<G, false, kTileInBlock>);
-    else if (mode == kShiftBlocks) go(paged_prefill_kernel<G, false, kShiftBlocks>);
-    else go(paged_prefill_kernel<G, false, kDivBlocks>);
-  }
+  auto pick = [&](auto fuse) {
+    constexpr bool F = decltype(fuse)::value;
+    if (pos) {
+      if (mode == kTileInBlock) go(paged_prefill_kernel<G, true, kTileInBlock, F>);
+      else if (mode == kShiftBlocks) go(paged_prefill_kernel<G, true, kShiftBlocks, F>);
+      else go(paged_prefill_kernel<G, true, kDivBlocks, F>);
+    } else {
+      if (mode == kTileInBlock) go(paged_prefill_kernel<G, false, kTileInBlock, F>);
+      else if (mode == kShiftBlocks) go(paged_prefill_kernel<G, false, kShiftBlocks, F>);
+      else go(paged_prefill_kernel<G, false, kDivBlocks, F>);
+    }
+  };
+  if (a.k_new) pick(std::true_type{});
+  else pick(std::false_type{});
   return hipGetLastError();
 }
 

@@ -196,3 +196,81 @@ def test_prefill_long_prefix_window(gpu_lib):
         x = prefill_case([50, window], [(1800, 300), (1000, 17)], bs=256, window=window)
         out, _ = run_store_prefill(gpu_lib, x)
         assert_close(out, oracle_prefill(x)[0])
+
+
+# ---- fused store + prefill (pk_paged_prefill_store) ---------------------------
+
+def run_fused(pk, x, max_seqlen_q=None):
+    """The fused entry on fresh copies of the inputs: (out, tensors)."""
+    t = to_torch(x, "cuda")
+    msq = max_seqlen_q or int(np.diff(x.cu_seqlens_q).max())
+    out = pk.paged_prefill_store(t["q"], t["key"], t["value"], t["k_cache"], t["v_cache"],
+                                 t["block_tables"], t["cu_seqlens_q"], t["cu_seqlens_k"], x.scale,
+                                 max_seqlen_q=msq, sliding_window=x.sliding_window)
+    return out, t
+
+
+def assert_fused_equals_unfused(pk, x):
+    """Output and both caches bit-identical to kv_store then paged_prefill."""
+    ref_out, tr = run_store_prefill(pk, x)
+    out, tf = run_fused(pk, x)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(tf["k_cache"].view(torch.int16), tr["k_cache"].view(torch.int16))
+    assert torch.equal(tf["v_cache"].view(torch.int16), tr["v_cache"].view(torch.int16))
+    return out, tf
+
+
+def test_prefill_store_workload(gpu_lib):
+    """The 16-sequence prefix workload: fused == store + prefill, bit for bit,
+    and both match the oracle (caches bit-exact)."""
+    x = W.prefix_prefill()
+    out, t = assert_fused_equals_unfused(gpu_lib, x)
+    ref, kc, vc = oracle_prefill(x)
+    assert np.array_equal(bits_of(t["k_cache"]), kc)
+    assert np.array_equal(bits_of(t["v_cache"]), vc)
+    assert_close(out, ref)
+
+
+@pytest.mark.parametrize("bs", [16, 32, 48, 64, 256])
+def test_prefill_store_block_sizes(gpu_lib, bs):
+    """Every block-addressing mode (division for 48, shifts below a tile,
+    tiles inside a block), prefixes off the tile grid."""
+    x = prefill_case([51, bs], SHAPES, bs=bs)
+    out, _ = assert_fused_equals_unfused(gpu_lib, x)
+    assert_close(out, oracle_prefill(x)[0])
+
+
+@pytest.mark.parametrize("window", [17, 256])
+def test_prefill_store_window(gpu_lib, window):
+    x = prefill_case([52, window], SHAPES, bs=64, window=window)
+    out, _ = assert_fused_equals_unfused(gpu_lib, x)
+    assert_close(out, oracle_prefill(x)[0])
+
+
+def test_prefill_store_mixed_and_empty(gpu_lib):
+    """The mixed decode + chunk batch, and sequences with no new tokens."""
+    assert_fused_equals_unfused(gpu_lib, W.mixed_batch())
+    assert_fused_equals_unfused(gpu_lib, prefill_case([53], [(10, 0), (0, 50), (64, 0), (30, 70)], bs=16))
+
+
+def test_prefill_store_bad_table_entry(gpu_lib):
+    """A block-table entry outside the cache inside a sequence's range: its
+    positions are neither stored nor attended, exactly as kv_store (which
+    skips the slot) then paged_prefill."""
+    x = prefill_case([54], [(40, 100), (0, 70)], bs=32, mb=6)
+    x.block_tables = x.block_tables.copy()
+    x.block_tables[0, 3] = x.k_cache.shape[0] + 5      # new positions 96..127 of sequence 0
+    x.block_tables[1, 0] = -7                          # new positions 0..31 of sequence 1
+    bad = np.zeros(len(x.slot_mapping), bool)
+    x.slot_mapping = x.slot_mapping.copy()
+    for b, (p, n) in enumerate([(40, 100), (0, 70)]):
+        q0 = int(x.cu_seqlens_q[b])
+        for i in range(n):
+            blk = x.block_tables[b, (p + i) // 32]
+            if not 0 <= blk < x.k_cache.shape[0]:
+                x.slot_mapping[q0 + i] = -1
+                bad[q0 + i] = True
+    assert bad.any()
+    out, _ = assert_fused_equals_unfused(gpu_lib, x)
+    assert torch.isfinite(out.float()).all()
