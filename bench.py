@@ -372,10 +372,24 @@ def mixed_leg(args, pk, W, dev, stream):
         pk.paged_prefill(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["cu_seqlens_q"],
                          t["cu_seqlens_k"], x.scale, max_seqlen_q=msq, out=out)
     us = time_call(run, stream, 10)
+    # The same step split by kind: the decode rows on the decode kernel, the
+    # chunks on the prefill kernel (two launches).
+    nd = int(np.sum(lq == 1))
+    mdcl = int(lk[:nd].max())
+    ws = torch.empty(max(pk.decode_workspace_size(nd, W.NUM_Q_HEADS, W.NUM_KV_HEADS, W.HEAD_DIM,
+                                                  mdcl), 1), dtype=torch.uint8, device=dev)
+
+    def run_split():
+        pk.paged_prefill_decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                t["cu_seqlens_q"], t["cu_seqlens_k"], x.scale, num_decode_seqs=nd,
+                                max_seqlen_q=int(lq[nd:].max()), max_decode_context_len=mdcl,
+                                out=out, workspace=ws)
+    us_split = time_call(run_split, stream, 10)
     flops = prefill_flops(lq, lk, W.NUM_Q_HEADS, W.HEAD_DIM)
     kv_bytes = int(lk.sum()) * W.NUM_KV_HEADS * W.HEAD_DIM * 2 * 2
     return {"workload": "chunked-prefill step: 48 decode seqs (ctx U{256..2048}) + 4 prefill chunks "
                         "(U{256..1024} new over 0-4 blocks), 4096-token budget",
+            "split_by_kind_us": round(us_split, 2),
             "total_q": int(lq.sum()), "us_per_launch": round(us, 2), "flops_per_launch": flops,
             "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 2),
             "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -212,6 +212,36 @@ pk_status pk_paged_prefill(void* out, const void* q,
                            int32_t num_q_heads, float scale, int32_t sliding_window,
                            void* stream);
 
+/* A mixed batch (chunked prefill: decode sequences and prefill chunks in one
+ * step, the step bounded by a token budget: nano-vllm-rs README, "Run
+ * Inference"; "How lunaryes/nano-vllm works", introduction) split by kind:
+ * the first num_decode_seqs sequences each have exactly one new token and
+ * run on the decode kernel (their K/V stream at decode's rate); the others
+ * run on the varlen prefill kernel.  Same result as pk_paged_prefill over the
+ * whole batch, within the attention tolerance (a different kernel's fp32
+ * summation order for the decode rows).
+ *   num_decode_seqs  leading sequences with one new token each (query row
+ *                    cu_seqlens_q[b]); a leading sequence with another count
+ *                    is left unwritten
+ *   max_seqlen_q     upper bound of the prefill sequences' query counts
+ *   max_decode_context_len  upper bound of the decode sequences' lengths
+ *                    (cu_seqlens_k differences); plans the decode split
+ *   workspace        as pk_paged_decode, sized by
+ *                    pk_paged_decode_workspace_size(num_decode_seqs, ...,
+ *                    max_decode_context_len, sliding_window, 0)
+ * Up to two launches on `stream` (decode rows, then the prefill).  Other
+ * arguments and errors as pk_paged_prefill; every argument is checked before
+ * either launch. */
+pk_status pk_paged_prefill_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                  int32_t num_blocks, int32_t block_size,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                  int32_t num_seqs, int32_t num_decode_seqs, int32_t total_q,
+                                  int32_t max_seqlen_q, int32_t max_decode_context_len,
+                                  int32_t num_q_heads, float scale, int32_t sliding_window,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Prefill with the new tokens' store fused in: the same result as
  * pk_kv_store of key/value at the slots of positions P_b .. P_b+Lq_b-1 of
  * each sequence (slot_mapping derived from block_tables) followed by

@@ -10,6 +10,7 @@ library has not been built, importing this package raises ImportError.
     paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ...)
     paged_prefill(q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k, scale, ...)
     paged_prefill_store(q, key, value, k_cache, v_cache, block_tables, cu_seqlens_q, ...)
+    paged_prefill_decode(q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k, ...)
     BlockManager(num_blocks, block_size)   host-side block allocation with prefix caching
 """
 from __future__ import annotations
@@ -23,7 +24,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "PagedKVError", "version", "kv_store", "paged_decode", "paged_decode_store",
-    "paged_prefill", "paged_prefill_store",
+    "paged_prefill", "paged_prefill_store", "paged_prefill_decode",
     "decode_plan", "decode_workspace_size", "BlockManager",
 ]
 
@@ -65,6 +66,9 @@ _lib.pk_paged_prefill.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i
 _lib.pk_paged_prefill_store.restype = ctypes.c_int
 _lib.pk_paged_prefill_store.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32,
                                         _p, _p, _i32, _i32, _i32, _i32, _f32, _i32, _p]
+_lib.pk_paged_prefill_decode.restype = ctypes.c_int
+_lib.pk_paged_prefill_decode.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p, _p,
+                                         _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]
 _i64 = ctypes.c_int64
 _pi32 = ctypes.POINTER(_i32)
 for _name, _args in (
@@ -313,6 +317,48 @@ def paged_prefill_store(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
         _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev),
         _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev),
         nseq, total_q, int(max_seqlen_q), hq, float(scale), sliding_window, _stream(dev)))
+    return out
+
+
+def paged_prefill_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_tables: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                         cu_seqlens_k: torch.Tensor, scale: float, *, num_decode_seqs: int,
+                         max_seqlen_q: int, max_decode_context_len: int, sliding_window: int = 0,
+                         out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A mixed batch whose first num_decode_seqs sequences have one new token
+    each: those on the decode kernel, the rest on the varlen prefill kernel."""
+    nb, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    dev = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [total_q, num_q_heads, head_dim]")
+    total_q, hq, qd = (int(x) for x in q.shape)
+    if qd != d:
+        raise ValueError("q and cache head_dim differ")
+    nseq = int(cu_seqlens_q.numel()) - 1
+    if nseq < 0 or cu_seqlens_k.shape != cu_seqlens_q.shape or block_tables.dim() != 2 \
+            or block_tables.shape[0] != nseq:
+        raise ValueError("cu_seqlens_q/k must be [num_seqs+1] and block_tables [num_seqs, max_blocks]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    nd = int(num_decode_seqs)
+    need = decode_workspace_size(nd, hq, hkv, d, int(max_decode_context_len), sliding_window) \
+        if nd > 0 else 0
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    ws_ptr = _dev(workspace, "workspace", torch.uint8, dev) if workspace is not None else None
+    ws_bytes = int(workspace.numel()) if workspace is not None else 0
+    _check(_lib.pk_paged_prefill_decode(
+        _dev(out, "out", torch.bfloat16, dev), _dev(q, "q", torch.bfloat16, dev),
+        _dev(k_cache, "k_cache", torch.bfloat16, dev), _dev(v_cache, "v_cache", torch.bfloat16, dev),
+        nb, bs, hkv, d,
+        _dev(block_tables, "block_tables", torch.int32, dev), int(block_tables.shape[1]),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev),
+        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev),
+        nseq, nd, total_q, int(max_seqlen_q), int(max_decode_context_len), hq, float(scale),
+        sliding_window, ws_ptr, ws_bytes, _stream(dev)))
     return out
 
 

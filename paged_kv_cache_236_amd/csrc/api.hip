@@ -141,7 +141,9 @@ static pk_status paged_decode_impl(void* out, const void* q, const void* k_cache
                           int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                           float scale, int32_t sliding_window, int32_t partition_size_request,
                           void* workspace, size_t workspace_bytes, void* stream,
-                          const void* k_new, const void* v_new) {
+                          const void* k_new, const void* v_new,
+                          const int32_t* cu_seqlens_q = nullptr,
+                          const int32_t* cu_seqlens_k = nullptr, int32_t total_rows = 0) {
   pk_status s = check_cache_shape(num_blocks, block_size, num_kv_heads, head_dim);
   if (s != PK_OK) return s;
   if ((s = check_heads(num_q_heads, num_kv_heads)) != PK_OK) return s;
@@ -153,7 +155,8 @@ static pk_status paged_decode_impl(void* out, const void* q, const void* k_cache
                        partition_size_request, &p)) != PK_OK)
     return s;
   if (num_seqs == 0) return ok();
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+  if (!out || !q || !k_cache || !v_cache || !block_tables ||
+      !(context_lens || (cu_seqlens_q && cu_seqlens_k)))
     return fail(PK_ERR_INVALID_ARG, "null pointer argument");
   const size_t need = workspace_bytes_for(num_seqs, num_q_heads, p);
   if (need > 0 && (!workspace || workspace_bytes < need))
@@ -191,6 +194,9 @@ static pk_status paged_decode_impl(void* out, const void* q, const void* k_cache
   a.length_order = p.num_parts == 1 && num_seqs <= kOrderMaxSeqs &&
                    num_seqs * num_kv_heads > kNumCUs;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.total_rows = total_rows;
   const hipError_t e = pk::launch_paged_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PK_ERR_LAUNCH, "paged_decode launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -369,6 +375,64 @@ pk_status pk_paged_prefill(void* out, const void* q, const void* k_cache, const 
                         num_kv_heads, head_dim, block_tables, max_blocks_per_seq, cu_seqlens_q,
                         cu_seqlens_k, num_seqs, total_q, max_seqlen_q, num_q_heads, scale,
                         sliding_window, false, stream);
+}
+
+pk_status pk_paged_prefill_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                  int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                                  int32_t head_dim, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                                  const int32_t* cu_seqlens_k, int32_t num_seqs,
+                                  int32_t num_decode_seqs, int32_t total_q, int32_t max_seqlen_q,
+                                  int32_t max_decode_context_len, int32_t num_q_heads, float scale,
+                                  int32_t sliding_window, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (num_seqs < 0 || num_decode_seqs < 0 || num_decode_seqs > num_seqs)
+    return fail(PK_ERR_INVALID_ARG, "need 0 <= num_decode_seqs <= num_seqs (got %d of %d)",
+                num_decode_seqs, num_seqs);
+  if (total_q < 0) return fail(PK_ERR_INVALID_ARG, "total_q must be >= 0 (got %d)", total_q);
+  if (max_decode_context_len < 0)
+    return fail(PK_ERR_INVALID_ARG, "max_decode_context_len must be >= 0 (got %d)",
+                max_decode_context_len);
+  if (num_seqs > 0 && (!cu_seqlens_q || !cu_seqlens_k || !block_tables))
+    return fail(PK_ERR_INVALID_ARG, "null pointer argument");
+  // Check both parts before launching either.
+  pk_status s = check_cache_shape(num_blocks, block_size, num_kv_heads, head_dim);
+  if (s != PK_OK) return s;
+  if ((s = check_heads(num_q_heads, num_kv_heads)) != PK_OK) return s;
+  if (max_blocks_per_seq <= 0 || max_blocks_per_seq > pk::kPrefillMaxBlocksPerSeq)
+    return fail(max_blocks_per_seq <= 0 ? PK_ERR_INVALID_ARG : PK_ERR_UNSUPPORTED,
+                "max_blocks_per_seq must be in [1, %d] (got %d)", pk::kPrefillMaxBlocksPerSeq,
+                max_blocks_per_seq);
+  Plan p;
+  if ((s = plan_decode(num_decode_seqs, num_kv_heads, max_decode_context_len, sliding_window, 0,
+                       &p)) != PK_OK)
+    return s;
+  const size_t need = workspace_bytes_for(num_decode_seqs, num_q_heads, p);
+  if (num_decode_seqs > 0 && need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PK_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  const int32_t rest = num_seqs - num_decode_seqs;
+  auto decode_part = [&](void* st) {
+    return paged_decode_impl(out, q, k_cache, v_cache, num_blocks, block_size, num_kv_heads,
+                             head_dim, block_tables, max_blocks_per_seq, nullptr, num_decode_seqs,
+                             num_q_heads, max_decode_context_len, scale, sliding_window, 0,
+                             workspace, workspace_bytes, st, nullptr, nullptr, cu_seqlens_q,
+                             cu_seqlens_k, total_q);
+  };
+  auto prefill_part = [&](void* st) {
+    return prefill_common(out, q, nullptr, nullptr, k_cache, v_cache, num_blocks, block_size,
+                          num_kv_heads, head_dim,
+                          block_tables + static_cast<int64_t>(num_decode_seqs) * max_blocks_per_seq,
+                          max_blocks_per_seq, cu_seqlens_q + num_decode_seqs,
+                          cu_seqlens_k + num_decode_seqs, rest, total_q, max_seqlen_q, num_q_heads,
+                          scale, sliding_window, false, st);
+  };
+  // Decode rows first, then the prefill, on the caller's stream.  (Running
+  // them side by side on two streams measured no faster: the two kernels did
+  // not overlap.)
+  if (num_decode_seqs > 0 && (s = decode_part(stream)) != PK_OK) return s;
+  if (rest > 0 && (s = prefill_part(stream)) != PK_OK) return s;
+  return ok();
 }
 
 pk_status pk_paged_prefill_store(void* out, const void* q, const void* key, const void* value,

@@ -46,6 +46,13 @@ struct DecodeArgs {
   int32_t num_parts;       // partition slots per sequence
   int32_t length_order;    // 1: workgroups take (seq, head) items longest-first, paired long/short
   float scale_log2;        // softmax scale * log2(e)
+  // Varlen form (decode rows of a mixed batch), or nullptr: sequence b's
+  // length is cu_seqlens_k[b+1] - cu_seqlens_k[b] (context_lens unused) and its
+  // q / out row is cu_seqlens_q[b] (< total_rows); a sequence without exactly
+  // one new token is not computed.
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int32_t total_rows;
 };
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -53,12 +53,23 @@ struct SeqRange {
   int L;        // admitted keys end (exclusive)
   int lo;       // admitted keys begin
   int nparts;   // partitions of the admitted keys (0 when L == 0)
+  int row;      // q / out row of the sequence; -1: not computed (varlen form only)
 };
+
+// Context length of sequence b (with its new token).
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int b) {
+  return a.cu_seqlens_k ? a.cu_seqlens_k[b + 1] - a.cu_seqlens_k[b] : a.context_lens[b];
+}
 
 __device__ __forceinline__ SeqRange seq_range(const DecodeArgs& a, int b) {
   SeqRange r;
   const int cap = min(a.max_blocks_per_seq * a.block_size, a.max_context_len);
-  r.L = min(max(a.context_lens[b], 0), cap);
+  r.L = min(max(seq_len(a, b), 0), cap);
+  r.row = b;
+  if (a.cu_seqlens_q) {
+    r.row = a.cu_seqlens_q[b];
+    if (a.cu_seqlens_q[b + 1] - r.row != 1 || r.row < 0 || r.row >= a.total_rows) r.row = -1;
+  }
   r.lo = a.sliding_window > 0 ? max(0, r.L - a.sliding_window) : 0;
   // Partitions start at lo (not at multiples of the partition size), so a
   // window of W keys takes ceil(W / partition_size) of them.
@@ -137,7 +148,7 @@ __device__ __forceinline__ void length_ordered_item(const DecodeArgs& a, int& b,
   // Unique keys, larger = earlier: length, then lower index first; 0 = no sequence.
   uint32_t key = 0;
   if (lane < B) {
-    const int L = min(max(a.context_lens[lane], 0), cap);
+    const int L = min(max(seq_len(a, lane), 0), cap);
     key = ((static_cast<uint32_t>(L) << 6) | static_cast<uint32_t>(63 - lane)) + 1u;
   }
   // Radix select of the key with exactly `target` keys above it, from the top
@@ -190,7 +201,8 @@ decode_partition_kernel(DecodeArgs a) {
                            pi * a.partition_size + wave * CT);
 
   const SeqRange r = seq_range(a, b);
-  uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(b) * hq + g * G) * kHeadDim;
+  if (r.row < 0) return;
+  uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(r.row) * hq + g * G) * kHeadDim;
   if (r.nparts == 0) {
     if (pi == 0)
       for (int o = threadIdx.x; o < G * kHeadDim; o += NW * kWave) out[o] = 0;
@@ -204,14 +216,14 @@ decode_partition_kernel(DecodeArgs a) {
   // q kept as packed bf16 pairs; the scale is applied to the reduced score.
   uint4 qp[G];
   {
-    const uint4* qv = static_cast<const uint4*>(a.q) + (static_cast<int64_t>(b) * hq + g * G) * 16 + col;
+    const uint4* qv = static_cast<const uint4*>(a.q) + (static_cast<int64_t>(r.row) * hq + g * G) * 16 + col;
 #pragma unroll
     for (int h = 0; h < G; ++h) qp[h] = qv[h * 16];
   }
 #else
   float qf[G][8];
   {
-    const uint4* qv = static_cast<const uint4*>(a.q) + (static_cast<int64_t>(b) * hq + g * G) * 16 + col;
+    const uint4* qv = static_cast<const uint4*>(a.q) + (static_cast<int64_t>(r.row) * hq + g * G) * 16 + col;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       unpack8(qv[h * 16], qf[h]);
@@ -424,7 +436,7 @@ decode_combine_kernel(DecodeArgs a) {
   const int g = blockIdx.x;
   const int b = blockIdx.y;
   const SeqRange r = seq_range(a, b);
-  if (r.nparts <= 1) return;   // written directly by the partition kernel
+  if (r.nparts <= 1 || r.row < 0) return;   // written directly by the partition kernel
   const int hq = a.num_kv_heads * G;
   const int h = threadIdx.x / kHeadDim;
   const int d = threadIdx.x % kHeadDim;
@@ -446,7 +458,7 @@ decode_combine_kernel(DecodeArgs a) {
     av = av * fo + ap * fn;
     mx = mn;
   }
-  static_cast<uint16_t*>(a.out)[head * kHeadDim + d] =
+  static_cast<uint16_t*>(a.out)[(static_cast<int64_t>(r.row) * hq + g * G + h) * kHeadDim + d] =
       static_cast<uint16_t>(f32_to_bf16_bits(ls > 0.f ? av / ls : 0.f));
 }
 

@@ -274,3 +274,78 @@ def test_prefill_store_bad_table_entry(gpu_lib):
     assert bad.any()
     out, _ = assert_fused_equals_unfused(gpu_lib, x)
     assert torch.isfinite(out.float()).all()
+
+
+# ---- mixed batch split by kind (pk_paged_prefill_decode) ---------------------
+
+def run_mixed(pk, x, nd, out=None):
+    t = to_torch(x, "cuda")
+    pk.kv_store(t["key"], t["value"], t["slot_mapping"], t["k_cache"], t["v_cache"])
+    lq = np.diff(x.cu_seqlens_q)
+    lk = np.diff(x.cu_seqlens_k)
+    res = pk.paged_prefill_decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                  t["cu_seqlens_q"], t["cu_seqlens_k"], x.scale,
+                                  num_decode_seqs=nd,
+                                  max_seqlen_q=int(lq[nd:].max()) if nd < len(lq) else 1,
+                                  max_decode_context_len=int(lk[:nd].max()) if nd else 0,
+                                  sliding_window=x.sliding_window, out=out)
+    return res, t
+
+
+def check_split_matches_parts(pk, x, nd):
+    """Decode rows bit-identical to pk_paged_decode of those sequences, the
+    other rows bit-identical to pk_paged_prefill of the remaining ones."""
+    out, t = run_mixed(pk, x, nd)
+    lk = np.diff(x.cu_seqlens_k)
+    if nd:
+        dec = pk.paged_decode(t["q"][:nd].contiguous(), t["k_cache"], t["v_cache"],
+                              t["block_tables"][:nd].contiguous(),
+                              torch.from_numpy(lk[:nd].astype(np.int32)).cuda(), x.scale,
+                              max_context_len=int(lk[:nd].max()), sliding_window=x.sliding_window)
+        assert torch.equal(out[:nd].view(torch.int16), dec.view(torch.int16))
+    if nd < x.num_seqs:
+        pre = pk.paged_prefill(t["q"], t["k_cache"], t["v_cache"], t["block_tables"][nd:].contiguous(),
+                               t["cu_seqlens_q"][nd:].contiguous(), t["cu_seqlens_k"][nd:].contiguous(),
+                               x.scale, max_seqlen_q=int(np.diff(x.cu_seqlens_q)[nd:].max()),
+                               sliding_window=x.sliding_window)
+        r0 = int(x.cu_seqlens_q[nd])
+        assert torch.equal(out[r0:].view(torch.int16), pre[r0:].view(torch.int16))
+    return out
+
+
+def test_mixed_split_workload(gpu_lib):
+    """The chunked-prefill step (48 decode rows + 4 chunks): decode rows on the
+    decode kernel, chunks on the prefill kernel, all within the bar of the oracle."""
+    x = W.mixed_batch()
+    nd = int(np.sum(np.diff(x.cu_seqlens_q) == 1))
+    assert nd == 48
+    out = check_split_matches_parts(gpu_lib, x, nd)
+    assert_close(out, oracle_prefill(x)[0])
+
+
+@pytest.mark.parametrize("window", [0, 100])
+def test_mixed_split_extremes_and_long(gpu_lib, window):
+    """All prefill, all decode, and decode contexts long enough to be split
+    over partitions (combine kernel, workspace) next to prefill chunks."""
+    shapes = [(5000, 1), (1, 1), (3000, 1), (700, 1), (0, 90), (300, 33)]
+    x = prefill_case([55, window], shapes, bs=64, window=window)
+    for nd in (0, 4):
+        out = check_split_matches_parts(gpu_lib, x, nd)
+        assert_close(out, oracle_prefill(x)[0])
+    y = prefill_case([56, window], shapes[:4], bs=64, window=window)
+    out = check_split_matches_parts(gpu_lib, y, 4)
+    assert_close(out, oracle_prefill(y)[0])
+
+
+def test_mixed_split_bad_leading_sequence_untouched(gpu_lib):
+    """A leading 'decode' sequence with two new tokens is left unwritten."""
+    x = prefill_case([57], [(50, 1), (60, 2), (70, 1), (0, 40)], bs=32)
+    t = to_torch(x, "cuda")
+    sentinel = torch.full_like(t["q"], 7.0)
+    out, _ = run_mixed(gpu_lib, x, 3, out=sentinel.clone())
+    rows = slice(int(x.cu_seqlens_q[1]), int(x.cu_seqlens_q[2]))
+    assert torch.equal(out[rows].view(torch.int16), sentinel[rows].view(torch.int16))
+    ref = oracle_prefill(x)[0]
+    keep = np.ones(len(ref), bool)
+    keep[rows] = False
+    assert_close(out, ref, rows=np.nonzero(keep)[0])
