@@ -112,6 +112,11 @@ def test_decode_plan_and_workspace(lib):
     assert (ps.value, n.value) == (256, 1)        # the planner's choice for the long-context window
     assert lib.pk_paged_decode_plan(64, 8, 8192, 1, 64, ctypes.byref(ps), ctypes.byref(n)) == OK
     assert n.value == 1
+    # few pairs: short contexts stay whole, longer ones split to fill the CUs
+    assert lib.pk_paged_decode_plan(8, 8, 128, 0, 0, ctypes.byref(ps), ctypes.byref(n)) == OK
+    assert (ps.value, n.value) == (128, 1)
+    assert lib.pk_paged_decode_plan(16, 8, 512, 0, 0, ctypes.byref(ps), ctypes.byref(n)) == OK
+    assert n.value > 1
     ws = lib.pk_paged_decode_workspace_size(64, 16, 8, 128, 8192, 0, 256)
     heads = 64 * 16 * 32
     assert ws >= heads * 130 * 4
