@@ -269,7 +269,8 @@ def main():
             "us_per_launch": round(launch_us, 2),
         },
         "unfused": {"paged_decode_us": round(dec_us, 2), "kv_store_us": round(store_us, 2),
-                    "paged_decode_GBps": round(dbytes / (dec_us * 1e-6) / 1e9, 1)},
+                    "paged_decode_GBps": round(dbytes / (dec_us * 1e-6) / 1e9, 1),
+                    "kv_store_GBps": round(sbytes / (store_us * 1e-6) / 1e9, 1)},
     }
 
     # ---- prefill leg ----------------------------------------------------------
@@ -307,6 +308,31 @@ def time_call(fn, stream, n):
     return e0.elapsed_time(e1) / n * 1e3
 
 
+_FLUSH = {}
+
+
+def time_cold(fn, stream, n):
+    """Median time of n single launches, each after writing a 512 MiB buffer
+    (twice the 256 MB MALL), so the launch finds none of its inputs cached."""
+    import torch
+    buf = _FLUSH.get("buf")
+    if buf is None:
+        buf = _FLUSH["buf"] = torch.empty(512 << 20, dtype=torch.uint8, device=torch.device("cuda:0"))
+    fn()
+    times = []
+    for _ in range(n):
+        buf.zero_()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    times.sort()
+    return times[len(times) // 2]
+
+
 def long_leg(args, pk, W, dev, stream):
     """64 seqs, context U{4096..8192}, block 256, 2 GiB cache: full and window 256."""
     import torch
@@ -328,6 +354,11 @@ def long_leg(args, pk, W, dev, stream):
         res["window_256" if window else "full"] = {
             "us_per_launch": round(us, 2), "bytes_per_launch": nbytes, "GB/s": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "partition_size": ps, "partitions_per_seq": nparts}
+        if window:
+            # 67 MB fit the MALL when launches repeat; cold: flushed before each.
+            us_cold = time_cold(run, stream, 11)
+            res["window_256"]["cold_us_per_launch"] = round(us_cold, 2)
+            res["window_256"]["cold_hbm_frac"] = round(nbytes / (us_cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
     return res
 
 
@@ -349,7 +380,11 @@ def small_leg(args, pk, W, dev, stream):
     us = time_call(lambda: pk.paged_decode_store(t["q"], t["key"], t["value"], t["k_cache"],
                                                  t["v_cache"], t["block_tables"], t["context_lens"],
                                                  y.scale, max_context_len=mcl), stream, 50)
+    run_store = lambda: pk.paged_decode_store(t["q"], t["key"], t["value"], t["k_cache"],
+                                              t["v_cache"], t["block_tables"], t["context_lens"],
+                                              y.scale, max_context_len=mcl)
     res["16seq_block256_store"] = {"us_per_launch": round(us, 2),
+                                   "cold_us_per_launch": round(time_cold(run_store, stream, 11), 2),
                                    "bytes_per_launch": decode_bytes(y.context_lens, 256, 16, 8, 128)
                                    + store_bytes(16, 8, 128)}
     return res
@@ -439,10 +474,14 @@ def prefill_leg(args, pk, W, dev, stream):
                                max_seqlen_q=msq, out=out)
     us_unfused = time_call(unfused, stream, n)
     us_fused = time_call(fused, stream, n)
+    us_store = time_call(lambda: pk.kv_store(t["key"], t["value"], t["slot_mapping"], t["k_cache"],
+                                             t["v_cache"]), stream, n)
+    sb = store_bytes(int(lq.sum()), W.NUM_KV_HEADS, W.HEAD_DIM)
     return {
         "workload": "varlen causal prefill, 16 seqs, new U{64..512}, prefix 0-2 x 256",
         "total_q": int(lq.sum()), "us_per_launch": round(us, 2), "flops_per_launch": flops,
         "store_then_prefill_us": round(us_unfused, 2), "fused_store_prefill_us": round(us_fused, 2),
+        "kv_store_us": round(us_store, 2), "kv_store_GBps": round(sb / (us_store * 1e-6) / 1e9, 1),
         "roofline": {"kernel": "paged_prefill_kernel", "bound": "mfma",
                      "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -47,7 +47,7 @@ def test_profiled_traffic_records_parse_and_track_sources(tmp_path, monkeypatch)
     b = _bench()
     with open(b.TRAFFIC_PROFILE) as fh:
         records = [l for l in fh.read().splitlines() if l.startswith("traffic-record:")]
-    assert {r.split()[1] for r in records} == {"decode_c64_fused", "prefill_prefix"}
+    assert {"decode_c64_fused", "prefill_prefix"} <= {r.split()[1] for r in records}
     for r in records:
         fields = dict(f.split("=", 1) for f in r.split()[2:])
         assert float(fields["fetch_kib"]) > 0 and len(fields["sources"]) == 16
