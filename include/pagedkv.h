@@ -53,7 +53,8 @@ typedef enum pk_status {
   PK_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent sizes */
   PK_ERR_UNSUPPORTED = 2,   /* a shape this build does not implement          */
   PK_ERR_WORKSPACE = 3,     /* decode workspace missing or too small           */
-  PK_ERR_LAUNCH = 4         /* the HIP runtime rejected a kernel launch        */
+  PK_ERR_LAUNCH = 4,        /* the HIP runtime rejected a kernel launch        */
+  PK_ERR_INDEX = 5          /* checked mode: index arrays violate a contract   */
 } pk_status;
 
 /* Library version string, e.g. "pagedkv 0.1.0 gfx950". */
@@ -264,6 +265,34 @@ pk_status pk_paged_prefill_store(void* out, const void* q, const void* key, cons
                                  int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
                                  int32_t num_q_heads, float scale, int32_t sliding_window,
                                  void* stream);
+
+/* ------------------------------------------------------------------------
+ * Checked mode.  The attention and store calls trust their index arrays (they
+ * bounds-check every access, so a bad index never touches memory outside the
+ * caches, but it changes the answer: a key with a bad block contributes
+ * nothing, a slot out of range is not stored, duplicate slots race).  This
+ * call validates them on the device, for debugging and tests, and writes
+ * violation counts to `counts` (device memory, 4 x int32, caller-owned):
+ *   counts[0]  slot_mapping entries outside [-1, num_blocks * block_size)
+ *   counts[1]  repeated slots (each occurrence of a slot >= 0 after its first)
+ *   counts[2]  block-table entries outside [0, num_blocks) in a sequence's
+ *              used range (entries past ceil(L / block_size) are not read)
+ *   counts[3]  sequences whose length is below 0 or beyond
+ *              max_blocks_per_seq * block_size, or (with cu_seqlens) whose
+ *              prefix sums decrease or have fewer keys than new queries
+ * Any of slot_mapping (num_tokens = 0) and the sequence arrays (num_seqs = 0)
+ * may be absent; lengths come from cu_seqlens_k when given, else from
+ * context_lens.  workspace: pk_check_indices_workspace_size bytes (a bitmap
+ * of the cache slots), cleared by the call itself (no memset).  Enqueued on
+ * `stream` like every call; read `counts` after synchronising.  The Python
+ * binding raises PK_ERR_INDEX when a count is not zero. */
+size_t pk_check_indices_workspace_size(int32_t num_blocks, int32_t block_size);
+pk_status pk_check_indices(const int32_t* slot_mapping, int32_t num_tokens,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t num_seqs, const int32_t* context_lens,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t num_blocks, int32_t block_size, int32_t* counts,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Host-side KV block manager (no GPU work).

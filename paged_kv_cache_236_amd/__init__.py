@@ -25,7 +25,7 @@ import torch
 __all__ = [
     "LIB_PATH", "PagedKVError", "version", "kv_store", "paged_decode", "paged_decode_store",
     "paged_prefill", "paged_prefill_store", "paged_prefill_decode",
-    "decode_plan", "decode_workspace_size", "BlockManager",
+    "decode_plan", "decode_workspace_size", "BlockManager", "check_indices",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
@@ -69,6 +69,10 @@ _lib.pk_paged_prefill_store.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32
 _lib.pk_paged_prefill_decode.restype = ctypes.c_int
 _lib.pk_paged_prefill_decode.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p, _p,
                                          _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p]
+_lib.pk_check_indices_workspace_size.restype = _sz
+_lib.pk_check_indices_workspace_size.argtypes = [_i32, _i32]
+_lib.pk_check_indices.restype = ctypes.c_int
+_lib.pk_check_indices.argtypes = [_p, _i32, _p, _i32, _i32, _p, _p, _p, _i32, _i32, _p, _p, _sz, _p]
 _i64 = ctypes.c_int64
 _pi32 = ctypes.POINTER(_i32)
 for _name, _args in (
@@ -360,6 +364,45 @@ def paged_prefill_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
         nseq, nd, total_q, int(max_seqlen_q), int(max_decode_context_len), hq, float(scale),
         sliding_window, ws_ptr, ws_bytes, _stream(dev)))
     return out
+
+
+PK_ERR_INDEX = 5
+CHECK_FIELDS = ("slots_out_of_range", "repeated_slots", "bad_table_entries", "bad_lengths")
+
+
+def check_indices(k_cache: torch.Tensor, *, slot_mapping: Optional[torch.Tensor] = None,
+                  block_tables: Optional[torch.Tensor] = None,
+                  context_lens: Optional[torch.Tensor] = None,
+                  cu_seqlens_q: Optional[torch.Tensor] = None,
+                  cu_seqlens_k: Optional[torch.Tensor] = None, raise_on_error: bool = True):
+    """Checked mode: validate the index arrays on the device against the cache
+    geometry of k_cache [num_blocks, block_size, Hkv, d]; returns the violation
+    counts (a dict), raising PagedKVError(PK_ERR_INDEX) when any is non-zero
+    and raise_on_error is set.  Synchronises the current stream."""
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [num_blocks, block_size, num_kv_heads, head_dim]")
+    nb, bs = int(k_cache.shape[0]), int(k_cache.shape[1])
+    dev = k_cache.device
+    nt = int(slot_mapping.numel()) if slot_mapping is not None else 0
+    if block_tables is not None:
+        if block_tables.dim() != 2:
+            raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+        nseq, mb = int(block_tables.shape[0]), int(block_tables.shape[1])
+    else:
+        nseq, mb = 0, 0
+    opt = lambda t, name: _dev(t, name, torch.int32, dev) if t is not None else None
+    counts = torch.empty(4, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(int(_lib.pk_check_indices_workspace_size(nb, bs)), 4), dtype=torch.uint8,
+                     device=dev)
+    _check(_lib.pk_check_indices(opt(slot_mapping, "slot_mapping"), nt,
+                                 opt(block_tables, "block_tables"), mb, nseq,
+                                 opt(context_lens, "context_lens"), opt(cu_seqlens_q, "cu_seqlens_q"),
+                                 opt(cu_seqlens_k, "cu_seqlens_k"), nb, bs, counts.data_ptr(),
+                                 ws.data_ptr(), int(ws.numel()), _stream(dev)))
+    res = dict(zip(CHECK_FIELDS, (int(v) for v in counts.cpu().tolist())))
+    if raise_on_error and any(res.values()):
+        raise PagedKVError(PK_ERR_INDEX, f"index arrays violate the contract: {res}")
+    return res
 
 
 def _host_i32(values, name: str) -> torch.Tensor:

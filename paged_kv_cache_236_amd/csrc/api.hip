@@ -221,6 +221,7 @@ const char* pk_status_string(pk_status s) {
     case PK_ERR_UNSUPPORTED: return "PK_ERR_UNSUPPORTED";
     case PK_ERR_WORKSPACE: return "PK_ERR_WORKSPACE";
     case PK_ERR_LAUNCH: return "PK_ERR_LAUNCH";
+    case PK_ERR_INDEX: return "PK_ERR_INDEX";
   }
   return "PK_ERR_UNKNOWN";
 }
@@ -382,6 +383,54 @@ pk_status pk_paged_prefill(void* out, const void* q, const void* k_cache, const 
                         num_kv_heads, head_dim, block_tables, max_blocks_per_seq, cu_seqlens_q,
                         cu_seqlens_k, num_seqs, total_q, max_seqlen_q, num_q_heads, scale,
                         sliding_window, false, stream);
+}
+
+size_t pk_check_indices_workspace_size(int32_t num_blocks, int32_t block_size) {
+  if (num_blocks <= 0 || block_size <= 0) {
+    fail(PK_ERR_INVALID_ARG, "num_blocks and block_size must be > 0");
+    return 0;
+  }
+  ok();
+  return static_cast<size_t>(pk::check_bitmap_words(num_blocks, block_size)) * sizeof(uint32_t);
+}
+
+pk_status pk_check_indices(const int32_t* slot_mapping, int32_t num_tokens,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t num_seqs, const int32_t* context_lens,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t num_blocks, int32_t block_size, int32_t* counts,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_blocks <= 0 || block_size <= 0)
+    return fail(PK_ERR_INVALID_ARG, "num_blocks and block_size must be > 0");
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq < 0)
+    return fail(PK_ERR_INVALID_ARG, "num_tokens, num_seqs and max_blocks_per_seq must be >= 0");
+  if (!counts) return fail(PK_ERR_INVALID_ARG, "counts must not be NULL");
+  if (num_tokens > 0 && !slot_mapping) return fail(PK_ERR_INVALID_ARG, "null slot_mapping");
+  if (num_seqs > 0 && (!block_tables || max_blocks_per_seq <= 0 || !(context_lens || cu_seqlens_k)))
+    return fail(PK_ERR_INVALID_ARG, "sequences need block_tables, max_blocks_per_seq > 0 and "
+                                    "context_lens or cu_seqlens_k");
+  const size_t need = static_cast<size_t>(pk::check_bitmap_words(num_blocks, block_size)) * sizeof(uint32_t);
+  if (!workspace || workspace_bytes < need)
+    return fail(PK_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0 || reinterpret_cast<uintptr_t>(counts) % 4 != 0)
+    return fail(PK_ERR_INVALID_ARG, "workspace and counts must be 4-byte aligned");
+  pk::CheckArgs a;
+  a.slot_mapping = num_tokens > 0 ? slot_mapping : nullptr;
+  a.block_tables = num_seqs > 0 ? block_tables : nullptr;
+  a.context_lens = context_lens;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.num_tokens = num_tokens;
+  a.num_seqs = num_seqs;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.counts = counts;
+  a.bitmap = static_cast<uint32_t*>(workspace);
+  const hipError_t e = pk::launch_check_indices(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PK_ERR_LAUNCH, "check_indices launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 pk_status pk_paged_prefill_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -80,4 +80,25 @@ struct PrefillArgs {
 };
 hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream);
 
+// Checked mode (index validation).
+constexpr int kCheckCounts = 4;
+inline int64_t check_bitmap_words(int32_t num_blocks, int32_t block_size) {
+  return (static_cast<int64_t>(num_blocks) * block_size + 31) / 32;
+}
+struct CheckArgs {
+  const int32_t* slot_mapping;   // [num_tokens] or nullptr
+  const int32_t* block_tables;   // [num_seqs, max_blocks_per_seq] or nullptr
+  const int32_t* context_lens;   // [num_seqs], used when cu_seqlens_k is nullptr
+  const int32_t* cu_seqlens_q;   // [num_seqs + 1] or nullptr
+  const int32_t* cu_seqlens_k;   // [num_seqs + 1] or nullptr
+  int32_t num_tokens;
+  int32_t num_seqs;
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t* counts;               // [kCheckCounts]
+  uint32_t* bitmap;              // [check_bitmap_words] one bit per cache slot
+};
+hipError_t launch_check_indices(const CheckArgs& a, hipStream_t stream);
+
 }  // namespace pk

@@ -150,3 +150,29 @@ def test_prefill_validation(lib, kw, status, text):
 
 def test_prefill_empty_is_ok(lib):
     assert prefill(lib, tq=0, q=None) == OK
+
+
+def test_check_indices_validation(lib):
+    lib.pk_check_indices_workspace_size.restype = ctypes.c_size_t
+    lib.pk_check_indices_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.pk_check_indices.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p] + [
+        ctypes.c_int32] * 2 + [ctypes.c_void_p] * 3 + [ctypes.c_int32] * 2 + [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert lib.pk_check_indices_workspace_size(64, 16) == 64 * 16 // 8
+    assert lib.pk_check_indices_workspace_size(1, 16) == 4
+    assert lib.pk_check_indices_workspace_size(0, 16) == 0 and "num_blocks" in msg(lib)
+
+    def call(**kw):
+        a = dict(slots=FAKE, nt=4, bt=FAKE, mb=2, nseq=3, ctx=FAKE, cq=None, ck=None, nb=8, bs=16,
+                 counts=FAKE, ws=FAKE, wsb=16)
+        a.update(kw)
+        return lib.pk_check_indices(a["slots"], a["nt"], a["bt"], a["mb"], a["nseq"], a["ctx"],
+                                    a["cq"], a["ck"], a["nb"], a["bs"], a["counts"], a["ws"],
+                                    a["wsb"], None)
+    assert call(counts=None) == INVALID and "counts" in msg(lib)
+    assert call(slots=None) == INVALID and "slot_mapping" in msg(lib)
+    assert call(ctx=None) == INVALID and "context_lens" in msg(lib)
+    assert call(nb=0) == INVALID
+    assert call(wsb=15) == WORKSPACE and "16 bytes" in msg(lib)
+    assert call(ws=None) == WORKSPACE
+    assert lib.pk_status_string(5) == b"PK_ERR_INDEX"
