@@ -525,6 +525,15 @@ paged_prefill_kernel(PrefillArgs a) {
     for (int kk = 0; kk < 8; ++kk)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kop[kk]), qreg[kk],
                                                   s, 0, 0, 0);
+    // All eight K reads first (left to itself the compiler issues them two at
+    // a time, each pair waiting out an LDS round trip before its products),
+    // then each S product followed by two of the V^T reads.
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
 
     // ---- online softmax over this lane's column ------------------------------
     // (16 keys of the tile in this lane, the other 16 in lane ^ 32)
