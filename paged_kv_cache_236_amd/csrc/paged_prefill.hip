@@ -666,20 +666,38 @@ paged_prefill_kernel(PrefillArgs a) {
   if constexpr (FUSE) st_load(st_first, tid >> 4);
 
   // ---- normalise and write ---------------------------------------------------
+  // The MFMA layout gives each lane one query row (column of O^T), so storing
+  // from registers would scatter 8-byte pieces over 32 output rows per
+  // instruction.  Instead each wavefront transposes its 32 rows x 256 bytes
+  // through LDS (one ring stage per wavefront, free once every wavefront has
+  // drained its DMAs and passed the barrier) and writes whole rows with
+  // 16-byte coalesced stores.  In LDS, 16-byte chunk c of row r sits at
+  // position c ^ (r % 16): the row-wise reads are conflict free and the
+  // column-wise writes at most 2-way.
   const float ltot = sum_xor32(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  if (qvalid) {
-    uint16_t* orow = static_cast<uint16_t*>(a.out) +
-                     (static_cast<int64_t>(q0 + qi) * hq + head) * kHeadDim;
+  __syncthreads();
+  char* const ot = wave == 0 ? s_k0 : wave == 1 ? s_k1 : wave == 2 ? s_k2 : s_k3;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int dim = mt * 32 + rg * 8 + hgrp * 4;
-        const uint2 v = make_uint2(pack_bf16x2(o[mt][rg * 4] * inv, o[mt][rg * 4 + 1] * inv),
-                                   pack_bf16x2(o[mt][rg * 4 + 2] * inv, o[mt][rg * 4 + 3] * inv));
-        *reinterpret_cast<uint2*>(orow + dim) = v;
-      }
+    for (int rg = 0; rg < 4; ++rg) {
+      const int ch = mt * 4 + rg;   // dims 8 ch .. 8 ch + 7; this lane holds half hgrp
+      const uint2 v = make_uint2(pack_bf16x2(o[mt][rg * 4] * inv, o[mt][rg * 4 + 1] * inv),
+                                 pack_bf16x2(o[mt][rg * 4 + 2] * inv, o[mt][rg * 4 + 3] * inv));
+      *reinterpret_cast<uint2*>(ot + c32 * kRow + (ch ^ (c32 & 15)) * 16 + hgrp * 8) = v;
+    }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4);      // row = this wavefront's column r
+    const uint4 v = *reinterpret_cast<const uint4*>(ot + r * kRow + (i16 ^ (r & 15)) * 16);
+    const int rcol = wave * 32 + r;
+    const int rqi = qa + rcol % BM;
+    if (rqi < Lq) {
+      uint16_t* orow = static_cast<uint16_t*>(a.out) +
+                       (static_cast<int64_t>(q0 + rqi) * hq + g * G + rcol / BM) * kHeadDim;
+      *reinterpret_cast<uint4*>(orow + i16 * 8) = v;
+    }
   }
 
   if constexpr (FUSE) {
