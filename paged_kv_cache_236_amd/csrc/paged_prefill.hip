@@ -129,7 +129,13 @@ __device__ __forceinline__ float sum_xor32(float x) {
 // table is only read during the kernel.
 __device__ __forceinline__ int32_t table_entry(const int32_t* row, int idx) {
   int32_t v;
-  const int32_t* p = row + idx;
+  // The address is wave-uniform; both halves go through readfirstlane so it
+  // sits in scalar registers whatever the compiler's uniformity analysis
+  // concluded (each half widened as unsigned: no sign extension).
+  const uint64_t pv = reinterpret_cast<uint64_t>(row + idx);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(pv))));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(pv >> 32))));
+  const int32_t* p = reinterpret_cast<const int32_t*>((static_cast<uint64_t>(hi) << 32) | lo);
   asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
   return v;
 }
@@ -254,9 +260,18 @@ paged_prefill_kernel(PrefillArgs a) {
   const int pr = static_cast<int>(blockIdx.x) % npairs;
   const int b = pr / a.num_kv_heads;
   const int g = pr % a.num_kv_heads;
-  const int q0 = a.cu_seqlens_q[b];
-  const int Lq = a.cu_seqlens_q[b + 1] - q0;
-  const int Lk = a.cu_seqlens_k[b + 1] - a.cu_seqlens_k[b];
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
+  // The sequence's lengths and its first block-table entry, fetched in one
+  // memory round trip: the empty asm needs all five values at once, so the
+  // compiler issues the five loads before a single wait (left alone it waits
+  // after each).  Without a window the first tile lies in block 0, so its
+  // DMAs need no further table lookup (the entry is judged like any other).
+  int q0 = a.cu_seqlens_q[b], q1 = a.cu_seqlens_q[b + 1];
+  int k0 = a.cu_seqlens_k[b], k1 = a.cu_seqlens_k[b + 1];
+  int blk_first = ONE ? bt[0] : 0;
+  asm volatile("" : "+s"(q0), "+s"(q1), "+s"(k0), "+s"(k1), "+s"(blk_first));
+  const int Lq = q1 - q0;
+  const int Lk = k1 - k0;
   const int P = Lk - Lq;
   const int qa = t * BM;
   if (Lq <= 0 || P < 0 || qa >= Lq || q0 < 0 || q0 + Lq > a.total_q) return;
@@ -265,7 +280,6 @@ paged_prefill_kernel(PrefillArgs a) {
   const int pos_lo = P + qa, pos_hi = P + qb - 1;
   const int kstart = W > 0 ? max(0, pos_lo - W + 1) : 0;
   const int tile0 = kstart / kBN, tile1 = pos_hi / kBN;
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
   const char* kcache = static_cast<const char*>(a.k_cache);
   const char* vcache = static_cast<const char*>(a.v_cache);
   const int64_t slot_bytes = static_cast<int64_t>(a.num_kv_heads) * kRow;
@@ -296,6 +310,12 @@ paged_prefill_kernel(PrefillArgs a) {
   int cur_lb = -1;
   int64_t cur_base = 0;
   bool cur_ok = false;
+  if constexpr (ONE) {
+    cur_lb = 0;
+    cur_ok = static_cast<unsigned>(blk_first) < static_cast<unsigned>(a.num_blocks);
+    cur_base = (cur_ok ? static_cast<int64_t>(blk_first) * a.block_size * slot_bytes : 0) +
+               static_cast<int64_t>(g) * kRow;
+  }
 
   // ---- DMA of one tile into ring stage ST (this wave's 8 K rows and 8 V rows)
   // Returns whether some row of the tile has a bad block entry (for a tile in
