@@ -81,7 +81,9 @@ def profiled_traffic(record: str, kernel_source: str):
     or None when the kernel's sources changed since the counters were taken."""
     import hashlib
     m = hashlib.sha256()
-    for f in (kernel_source, "device_common.h", "launch.h", "api.hip"):
+    kernel_header = {"paged_decode.hip": "decode_kernel.h",
+                     "paged_prefill.hip": "prefill_kernel.h"}[kernel_source]
+    for f in (kernel_source, kernel_header, "device_common.h", "launch.h", "api.hip"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             m.update(fh.read())
     digest = m.hexdigest()[:16]

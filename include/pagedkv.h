@@ -230,9 +230,14 @@ pk_status pk_paged_prefill(void* out, const void* q,
  *   workspace        as pk_paged_decode, sized by
  *                    pk_paged_decode_workspace_size(num_decode_seqs, ...,
  *                    max_decode_context_len, sliding_window, 0)
- * Up to two launches on `stream` (decode rows, then the prefill).  Other
- * arguments and errors as pk_paged_prefill; every argument is checked before
- * either launch. */
+ * One launch on `stream` when the shapes allow it: its workgroups are the
+ * prefill's heaviest query tiles, then the decode rows, then the rest of the
+ * prefill, so the decode rows stream while the long prefill chains compute.
+ * That needs a power-of-two block_size >= 32, one decode partition per
+ * sequence and both kinds present.  Otherwise it makes two launches (decode
+ * rows, then the prefill).  Either way each row's result is bit-identical to
+ * the separate kernels.  Other arguments and errors as pk_paged_prefill;
+ * every argument is checked before any launch. */
 pk_status pk_paged_prefill_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                                   int32_t num_blocks, int32_t block_size,
                                   int32_t num_kv_heads, int32_t head_dim,

@@ -150,7 +150,8 @@ static pk_status paged_decode_impl(void* out, const void* q, const void* k_cache
                           void* workspace, size_t workspace_bytes, void* stream,
                           const void* k_new, const void* v_new,
                           const int32_t* cu_seqlens_q = nullptr,
-                          const int32_t* cu_seqlens_k = nullptr, int32_t total_rows = 0) {
+                          const int32_t* cu_seqlens_k = nullptr, int32_t total_rows = 0,
+                          pk::DecodeArgs* capture = nullptr) {
   pk_status s = check_cache_shape(num_blocks, block_size, num_kv_heads, head_dim);
   if (s != PK_OK) return s;
   if ((s = check_heads(num_q_heads, num_kv_heads)) != PK_OK) return s;
@@ -204,6 +205,10 @@ static pk_status paged_decode_impl(void* out, const void* q, const void* k_cache
   a.cu_seqlens_q = cu_seqlens_q;
   a.cu_seqlens_k = cu_seqlens_k;
   a.total_rows = total_rows;
+  if (capture) {   // checked and built, launched by the caller
+    *capture = a;
+    return ok();
+  }
   const hipError_t e = pk::launch_paged_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PK_ERR_LAUNCH, "paged_decode launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -322,7 +327,7 @@ pk_status prefill_common(void* out, const void* q, const void* k_new, const void
                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                          int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
                          int32_t num_q_heads, float scale, int32_t sliding_window, bool fused,
-                         void* stream) {
+                         void* stream, pk::PrefillArgs* capture = nullptr) {
   pk_status s = check_cache_shape(num_blocks, block_size, num_kv_heads, head_dim);
   if (s != PK_OK) return s;
   if ((s = check_heads(num_q_heads, num_kv_heads)) != PK_OK) return s;
@@ -363,6 +368,10 @@ pk_status prefill_common(void* out, const void* q, const void* k_new, const void
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.sliding_window = sliding_window;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
+  if (capture) {   // checked and built, launched by the caller
+    *capture = a;
+    return ok();
+  }
   const hipError_t e = pk::launch_paged_prefill(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported)
     return fail(PK_ERR_UNSUPPORTED, "paged_prefill: this configuration is not implemented");
@@ -468,26 +477,37 @@ pk_status pk_paged_prefill_decode(void* out, const void* q, const void* k_cache,
     return fail(PK_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : static_cast<size_t>(0));
   const int32_t rest = num_seqs - num_decode_seqs;
-  auto decode_part = [&](void* st) {
+  auto decode_part = [&](void* st, pk::DecodeArgs* capture) {
     return paged_decode_impl(out, q, k_cache, v_cache, num_blocks, block_size, num_kv_heads,
                              head_dim, block_tables, max_blocks_per_seq, nullptr, num_decode_seqs,
                              num_q_heads, max_decode_context_len, scale, sliding_window, 0,
                              workspace, workspace_bytes, st, nullptr, nullptr, cu_seqlens_q,
-                             cu_seqlens_k, total_q);
+                             cu_seqlens_k, total_q, capture);
   };
-  auto prefill_part = [&](void* st) {
+  auto prefill_part = [&](void* st, pk::PrefillArgs* capture) {
     return prefill_common(out, q, nullptr, nullptr, k_cache, v_cache, num_blocks, block_size,
                           num_kv_heads, head_dim,
                           block_tables + static_cast<int64_t>(num_decode_seqs) * max_blocks_per_seq,
                           max_blocks_per_seq, cu_seqlens_q + num_decode_seqs,
                           cu_seqlens_k + num_decode_seqs, rest, total_q, max_seqlen_q, num_q_heads,
-                          scale, sliding_window, false, st);
+                          scale, sliding_window, false, st, capture);
   };
-  // Decode rows first, then the prefill, on the caller's stream.  (Running
-  // them side by side on two streams measured no faster: the two kernels did
-  // not overlap.)
-  if (num_decode_seqs > 0 && (s = decode_part(stream)) != PK_OK) return s;
-  if (rest > 0 && (s = prefill_part(stream)) != PK_OK) return s;
+  // Both kinds in one launch when the combined kernel covers the shapes (the
+  // prefill's long chains and the decode rows' streaming then overlap),
+  // else the decode rows and then the prefill on the caller's stream.
+  // (Two streams measured no faster: the two kernels did not overlap.)
+  if (num_decode_seqs > 0 && rest > 0 && total_q > 0 && max_seqlen_q > 0) {
+    pk::DecodeArgs da;
+    pk::PrefillArgs pa;
+    if ((s = decode_part(stream, &da)) != PK_OK) return s;
+    if ((s = prefill_part(stream, &pa)) != PK_OK) return s;
+    const hipError_t e = pk::launch_mixed_batch(pa, da, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) return ok();
+    if (e != hipErrorNotSupported)
+      return fail(PK_ERR_LAUNCH, "mixed batch launch failed: %s", hipGetErrorString(e));
+  }
+  if (num_decode_seqs > 0 && (s = decode_part(stream, nullptr)) != PK_OK) return s;
+  if (rest > 0 && (s = prefill_part(stream, nullptr)) != PK_OK) return s;
   return ok();
 }
 

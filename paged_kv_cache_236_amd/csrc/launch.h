@@ -80,6 +80,12 @@ struct PrefillArgs {
 };
 hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream);
 
+// A mixed batch in one launch: prefill work items of `p` first, then the
+// decode items of `d` (one partition per sequence).  hipErrorNotSupported
+// (nothing launched) when the configuration is not the one the combined
+// kernel covers; the caller then launches the two kinds separately.
+hipError_t launch_mixed_batch(const PrefillArgs& p, const DecodeArgs& d, hipStream_t stream);
+
 // Checked mode (index validation).
 constexpr int kCheckCounts = 4;
 inline int64_t check_bitmap_words(int32_t num_blocks, int32_t block_size) {

@@ -337,6 +337,17 @@ def test_mixed_split_extremes_and_long(gpu_lib, window):
     assert_close(out, oracle_prefill(y)[0])
 
 
+@pytest.mark.parametrize("bs", [16, 32, 256])
+def test_mixed_split_block_sizes(gpu_lib, bs):
+    """Decode rows in one partition next to prefill chunks: one combined launch
+    for power-of-two blocks of >= 32 keys, two launches for block 16; either
+    way bit-identical to the separate kernels and within the oracle's bar."""
+    shapes = [(300, 1), (40, 1), (700, 1), (129, 1), (100, 200), (0, 77), (513, 64)]
+    x = prefill_case([58, bs], shapes, bs=bs)
+    out = check_split_matches_parts(gpu_lib, x, 4)
+    assert_close(out, oracle_prefill(x)[0])
+
+
 def test_mixed_split_bad_leading_sequence_untouched(gpu_lib):
     """A leading 'decode' sequence with two new tokens is left unwritten."""
     x = prefill_case([57], [(50, 1), (60, 2), (70, 1), (0, 40)], bs=32)
