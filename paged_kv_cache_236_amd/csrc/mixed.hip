@@ -10,8 +10,6 @@
 // after the other.  Each workgroup runs the same code as the separate kernel
 // of its kind (prefill_kernel.h, decode_kernel.h), so the results are
 // bit-identical to those launches.
-#include <algorithm>
-
 #include "decode_kernel.h"
 #include "prefill_kernel.h"
 
