@@ -198,9 +198,12 @@ static pk_status paged_decode_impl(void* out, const void* q, const void* k_cache
   a.num_parts = p.num_parts;
   // Length ordering pays when each (seq, KV head) item is one workgroup and
   // there are more items than CUs (several items share a CU); the in-kernel
-  // ranking handles up to one wavefront of sequences.
+  // ranking handles up to one wavefront of sequences.  With a window the
+  // context length no longer measures an item's work (every long sequence
+  // admits W keys), so the ranking is skipped (measured 2 % faster on 64
+  // sequences of 4096-8192 keys with a 256-key window).
   a.length_order = p.num_parts == 1 && num_seqs <= kOrderMaxSeqs &&
-                   num_seqs * num_kv_heads > kNumCUs;
+                   num_seqs * num_kv_heads > kNumCUs && sliding_window == 0;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
   a.cu_seqlens_q = cu_seqlens_q;
   a.cu_seqlens_k = cu_seqlens_k;
