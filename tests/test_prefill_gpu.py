@@ -348,6 +348,16 @@ def test_mixed_split_block_sizes(gpu_lib, bs):
     assert_close(out, oracle_prefill(x)[0])
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 8), (64, 8)])
+def test_mixed_split_group_sizes(gpu_lib, hq, hkv):
+    """The combined launch for every head grouping it is built for (1, 4, 8 query
+    heads per KV head; 2 is the workload above)."""
+    shapes = [(200, 1), (517, 1), (64, 1), (100, 150), (0, 70)]
+    x = prefill_case([59, hq], shapes, bs=64, hq=hq, hkv=hkv)
+    out = check_split_matches_parts(gpu_lib, x, 3)
+    assert_close(out, oracle_prefill(x)[0])
+
+
 def test_mixed_split_bad_leading_sequence_untouched(gpu_lib):
     """A leading 'decode' sequence with two new tokens is left unwritten."""
     x = prefill_case([57], [(50, 1), (60, 2), (70, 1), (0, 40)], bs=32)
