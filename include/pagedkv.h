@@ -234,7 +234,7 @@ pk_status pk_paged_prefill(void* out, const void* q,
  * prefill's heaviest query tiles, then the decode rows, then the rest of the
  * prefill, so the decode rows stream while the long prefill chains compute.
  * That needs a power-of-two block_size >= 32, one decode partition per
- * sequence and both kinds present.  Otherwise it makes two launches (decode
+ * sequence, at most 4 query heads per KV head and both kinds present.  Otherwise it makes two launches (decode
  * rows, then the prefill).  Either way each row's result is bit-identical to
  * the separate kernels.  Other arguments and errors as pk_paged_prefill;
  * every argument is checked before any launch. */

@@ -64,14 +64,16 @@ hipError_t launch_group(const PrefillArgs& p, const DecodeArgs& d, int64_t prefi
 hipError_t launch_mixed_batch(const PrefillArgs& p, const DecodeArgs& d, hipStream_t stream) {
   // The combined kernel covers the common case: tiles inside one cache block
   // (power-of-two block of >= 32 keys), no fused store, the decode rows in one
-  // partition each with 16-token chunks, and the same head grouping.
+  // partition each with 16-token chunks, and the same head grouping.  Eight
+  // query heads per KV head are left to two launches: the decode body then
+  // needs 336 registers and 82 KiB of LDS, one workgroup per CU.
   const int BM = kCols / (p.group > 0 ? p.group : 1);
   const int64_t ntiles = (p.max_seqlen_q + BM - 1) / BM;
   const int64_t prefill_groups = ntiles * p.num_seqs * p.num_kv_heads;
   const int64_t decode_groups = static_cast<int64_t>(d.num_seqs) * d.num_kv_heads;
   const bool in_block = p.block_shift >= 0 && p.block_size >= kBN &&
                         static_cast<int64_t>(p.block_size) * p.num_kv_heads * kRow < (int64_t{1} << 31);
-  if (!in_block || p.k_new || d.k_new || d.num_parts != 1 || p.group != d.group ||
+  if (!in_block || p.k_new || d.k_new || d.num_parts != 1 || p.group != d.group || p.group > 4 ||
       kDecodeLoads != 4 || d.block_size % 16 != 0 || prefill_groups <= 0 || decode_groups <= 0 ||
       prefill_groups + decode_groups > 0x7fffffff)
     return hipErrorNotSupported;
@@ -79,7 +81,6 @@ hipError_t launch_mixed_batch(const PrefillArgs& p, const DecodeArgs& d, hipStre
     case 1: return launch_group<1>(p, d, prefill_groups, decode_groups, stream);
     case 2: return launch_group<2>(p, d, prefill_groups, decode_groups, stream);
     case 4: return launch_group<4>(p, d, prefill_groups, decode_groups, stream);
-    case 8: return launch_group<8>(p, d, prefill_groups, decode_groups, stream);
     default: return hipErrorNotSupported;
   }
 }
