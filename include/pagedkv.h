@@ -122,8 +122,11 @@ size_t pk_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *
  *   out           bf16 [num_seqs, num_q_heads, head_dim]
  *   q             bf16 [num_seqs, num_q_heads, head_dim]
- *   block_tables  int32 [num_seqs, max_blocks_per_seq]; entries past
- *                 ceil(context_lens[b] / block_size) are never read
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]; only the entries of
+ *                 a sequence's admitted range address cache rows.  Other
+ *                 entries of the row may be read (e.g. ahead of the length),
+ *                 but their values are never used as block ids, so they may
+ *                 hold anything (padding such as -1 or INT32_MAX)
  *   context_lens  int32 [num_seqs]; L_b keys, including the new token, which
  *                 is the query (it must already be stored, e.g. by
  *                 pk_kv_store earlier on the same stream).  Values are clamped
@@ -161,6 +164,11 @@ pk_status pk_paged_decode(void* out, const void* q,
  * pk_paged_decode over positions lo..L_b-1 with position L_b - 1 taken from
  * k_new / v_new.  Results and caches are bit-identical to pk_kv_store with
  * slot_mapping[b] = slot of position L_b - 1 followed by pk_paged_decode.
+ * L_b is the caller's context length, not clamped: when L_b exceeds
+ * max_context_len, the row is still stored at position L_b - 1 (if the table
+ * has an entry for it) but attention covers only the clamped range, as it
+ * would after pk_kv_store; when L_b - 1 lies beyond the table row, nothing is
+ * stored (no slot exists for it).
  * (The fused kernel the nano-vllm-sansho README names as an optimization
  * target, "Sansho Serving Roofline Anchors".)  Other arguments, workspace
  * sizing and errors as pk_paged_decode.  A block-table entry outside the cache
@@ -319,9 +327,15 @@ pk_status pk_check_indices(const int32_t* slot_mapping, int32_t num_tokens,
  *    holds stays cached until its space is handed out again, least recently
  *    freed first;
  *  - only full blocks are shared, so every slot a call writes belongs to one
- *    sequence.
- * A hit may name a block that another sequence of the same batch is about to
- * fill: its K/V are stored (pk_kv_store) before any attention call reads them.
+ *    sequence;
+ *  - a block that becomes full (at pk_bm_allocate or pk_bm_append) is pending
+ *    until the next pk_bm_commit and is not found by pk_bm_allocate before
+ *    then.  Its K/V are written by the step the caller runs next, so no batch
+ *    is ever handed a cached prefix block that the same batch writes: every
+ *    call, pk_paged_prefill_store and pk_paged_decode_store included, reads
+ *    only prefix rows stored by an earlier, already enqueued step.
+ * Typical step: allocate / append / free, pk_bm_prepare, enqueue the step's
+ * store and attention calls, then pk_bm_commit.
  * A manager is not thread-safe: one thread (the scheduler) owns it.  Errors
  * return a non-OK status, set pk_last_error_message(), and leave the manager
  * unchanged; PK_ERR_WORKSPACE means the free blocks do not suffice.
@@ -338,21 +352,28 @@ void pk_bm_destroy(pk_block_manager* m);
 pk_status pk_bm_num_free_blocks(const pk_block_manager* m, int32_t* out);
 
 /* How many sequences hold `block`, and whether its content is registered
- * (findable by prefix hash). */
+ * (committed, so findable by prefix hash; a pending block reports 0). */
 pk_status pk_bm_block_info(const pk_block_manager* m, int32_t block, int32_t* ref_count,
                            int32_t* cached);
 
 /* Admit sequence `seq_id` (unused so far) with its prompt tokens[0..n) (host
  * memory, n >= 1).  *num_cached_tokens receives how many leading tokens reuse
- * cached blocks (a multiple of block_size, < n): only tokens from there on
- * need K/V computed and stored.  The prompt's full blocks become findable by
- * later calls at once. */
+ * committed blocks (a multiple of block_size, < n): only tokens from there on
+ * need K/V computed and stored.  The prompt's other full blocks are pending
+ * until the next pk_bm_commit. */
 pk_status pk_bm_allocate(pk_block_manager* m, int64_t seq_id, const int32_t* tokens,
                          int32_t num_tokens, int32_t* num_cached_tokens);
 
 /* Append one generated token to `seq_id`; takes a new block when the token
- * opens one and registers a block that it fills. */
+ * opens one, and a block that it fills becomes pending. */
 pk_status pk_bm_append(pk_block_manager* m, int64_t seq_id, int32_t token);
+
+/* Make every pending block findable by later pk_bm_allocate calls.  Call it
+ * once the step that stores those blocks' K/V has been enqueued (on the stream
+ * that later attention calls use).  A pending block whose sequence was freed
+ * in the meantime is dropped, not registered.  *num_registered (may be NULL)
+ * receives how many blocks became findable. */
+pk_status pk_bm_commit(pk_block_manager* m, int32_t* num_registered);
 
 /* Drop `seq_id` and its block references (last block first). */
 pk_status pk_bm_free(pk_block_manager* m, int64_t seq_id);

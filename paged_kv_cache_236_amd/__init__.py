@@ -81,6 +81,7 @@ for _name, _args in (
         ("pk_bm_block_info", [_p, _i32, _pi32, _pi32]),
         ("pk_bm_allocate", [_p, _i64, _p, _i32, _pi32]),
         ("pk_bm_append", [_p, _i64, _i32]),
+        ("pk_bm_commit", [_p, _pi32]),
         ("pk_bm_free", [_p, _i64]),
         ("pk_bm_seq_info", [_p, _i64, _pi32, _pi32, _pi32]),
         ("pk_bm_prepare", [_p, _p, _i32, _p, _i32, _p, _p, _p, _p])):
@@ -419,7 +420,9 @@ class BlockManager:
     slots.  ``allocate`` admits a sequence and returns how many leading prompt
     tokens reuse cached blocks; ``append`` adds a generated token; ``free``
     drops a sequence; ``prepare`` returns the int32 CPU tensors one attention
-    call needs (block_tables, cu_seqlens_q, cu_seqlens_k, slot_mapping).
+    call needs (block_tables, cu_seqlens_q, cu_seqlens_k, slot_mapping);
+    ``commit`` ends a step: blocks filled during it become findable only then,
+    so a batch never reuses a prefix block that the same batch writes.
     """
 
     def __init__(self, num_blocks: int, block_size: int):
@@ -468,6 +471,14 @@ class BlockManager:
 
     def append(self, seq_id: int, token: int) -> None:
         _check(_lib.pk_bm_append(self._handle(), int(seq_id), int(token)))
+
+    def commit(self) -> int:
+        """Make the blocks filled since the last commit findable by later
+        ``allocate`` calls; call it once the step that stores their K/V has
+        been enqueued.  Returns how many blocks became findable."""
+        n = _i32()
+        _check(_lib.pk_bm_commit(self._handle(), ctypes.byref(n)))
+        return n.value
 
     def free(self, seq_id: int) -> None:
         _check(_lib.pk_bm_free(self._handle(), int(seq_id)))

@@ -18,7 +18,13 @@
 //    joins the back of the free queue while staying findable by hash until its
 //    space is handed out again (least recently freed first);
 //  * a decode step appends one token: a sequence that crosses a block boundary
-//    gets a new block, and a block that becomes full is registered by hash.
+//    gets a new block, and a block that becomes full gets its hash;
+//  * a block that became full is pending until pk_bm_commit: its K/V are
+//    computed and stored by the step the caller is about to run, so a hit on
+//    it in the same step would read rows not yet written (the fused store +
+//    prefill writes them inside the very launch that reads the prefix).  The
+//    commit, called once the step's kernels are enqueued, makes the pending
+//    blocks findable; a pending block that is freed first is dropped.
 // Only full blocks are ever shared, so the block a token is written to belongs
 // to one sequence.  Host code only: nothing here touches the GPU.
 #include <stdint.h>
@@ -60,10 +66,11 @@ uint64_t chain_hash(uint64_t prev, const int32_t* tokens, int32_t n) {
 
 struct Block {
   int32_t ref = 0;
-  uint64_t hash = kNoHash;
+  uint64_t hash = kNoHash;        // chain hash of a full block (pending or registered)
   uint32_t gen = 0;               // bumped each time the block joins the free queue
   bool free = true;
-  std::vector<int32_t> tokens;    // token ids of a registered block
+  bool pending = false;           // full, hashed, not yet findable (waits for pk_bm_commit)
+  std::vector<int32_t> tokens;    // token ids of a full block
 };
 
 struct Seq {
@@ -86,6 +93,7 @@ struct pk_block_manager {
   // to every holder and evicting one leaves the others findable.
   std::unordered_map<uint64_t, std::vector<int32_t>> by_hash;
   std::unordered_map<int64_t, pk::Seq> seqs;
+  std::vector<int32_t> pending;   // blocks filled since the last commit, in fill order
 };
 
 namespace pk {
@@ -101,6 +109,13 @@ bool live_entry(const pk_block_manager* m, const std::pair<int32_t, uint32_t>& e
 
 void push_free(pk_block_manager* m, int32_t b) {
   Block& blk = m->blocks[b];
+  if (blk.pending) {
+    // Freed before its step was committed: its rows may never have been
+    // written, so it is not offered for reuse (pk_bm_commit skips it).
+    blk.pending = false;
+    blk.hash = kNoHash;
+    blk.tokens.clear();
+  }
   blk.free = true;
   ++blk.gen;
   ++m->num_free;
@@ -170,8 +185,9 @@ int32_t lookup(const pk_block_manager* m, uint64_t h, const int32_t* tokens) {
   return found;
 }
 
-// Register block `index` of `s`, which has just become (or was born) full.
-void register_full(pk_block_manager* m, Seq& s, int32_t index) {
+// Hash block `index` of `s`, which has just become (or was born) full, and
+// queue it for the next commit (the sequence's chain continues from it at once).
+void fill_full(pk_block_manager* m, Seq& s, int32_t index) {
   const int32_t b = s.blocks[index];
   Block& blk = m->blocks[b];
   const uint64_t prev = index > 0 ? s.hashes[index - 1] : 0;
@@ -180,7 +196,8 @@ void register_full(pk_block_manager* m, Seq& s, int32_t index) {
   s.hashes.push_back(h);
   blk.hash = h;
   blk.tokens.assign(t, t + m->block_size);
-  m->by_hash[h].push_back(b);
+  blk.pending = true;
+  m->pending.push_back(b);
 }
 
 const Seq* find_seq(const pk_block_manager* m, int64_t id) {
@@ -223,8 +240,9 @@ pk_status pk_bm_block_info(const pk_block_manager* m, int32_t block, int32_t* re
   if (!m || !ref_count || !cached) return pk::fail(PK_ERR_INVALID_ARG, "NULL argument");
   if (block < 0 || block >= static_cast<int32_t>(m->blocks.size()))
     return pk::fail(PK_ERR_INVALID_ARG, "block index out of range");
-  *ref_count = m->blocks[block].ref;
-  *cached = m->blocks[block].hash != pk::kNoHash;
+  const pk::Block& blk = m->blocks[block];
+  *ref_count = blk.ref;
+  *cached = blk.hash != pk::kNoHash && !blk.pending;
   return pk::ok();
 }
 
@@ -268,7 +286,7 @@ pk_status pk_bm_allocate(pk_block_manager* m, int64_t seq_id, const int32_t* tok
   }
   s.num_cached = static_cast<int32_t>(hits.size()) * bs;
   for (int32_t i = 0; i < fresh; ++i) s.blocks.push_back(pk::take_free(m));
-  for (int32_t i = static_cast<int32_t>(hits.size()); i < nfull; ++i) pk::register_full(m, s, i);
+  for (int32_t i = static_cast<int32_t>(hits.size()); i < nfull; ++i) pk::fill_full(m, s, i);
   *num_cached_tokens = s.num_cached;
   return pk::ok();
 }
@@ -287,7 +305,22 @@ pk_status pk_bm_append(pk_block_manager* m, int64_t seq_id, int32_t token) {
     s.blocks.push_back(b);
   }
   s.tokens.push_back(token);
-  if ((n + 1) % bs == 0) pk::register_full(m, s, static_cast<int32_t>(n / bs));
+  if ((n + 1) % bs == 0) pk::fill_full(m, s, static_cast<int32_t>(n / bs));
+  return pk::ok();
+}
+
+pk_status pk_bm_commit(pk_block_manager* m, int32_t* num_registered) {
+  if (!m) return pk::fail(PK_ERR_INVALID_ARG, "NULL manager");
+  int32_t n = 0;
+  for (int32_t b : m->pending) {
+    pk::Block& blk = m->blocks[b];
+    if (!blk.pending) continue;   // freed (and possibly reused) since it was filled
+    blk.pending = false;
+    m->by_hash[blk.hash].push_back(b);
+    ++n;
+  }
+  m->pending.clear();
+  if (num_registered) *num_registered = n;
   return pk::ok();
 }
 

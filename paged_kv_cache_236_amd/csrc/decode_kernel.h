@@ -206,9 +206,44 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
   const SeqRange r = seq_range(a, b);
   if (r.row < 0) return;
   uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(r.row) * hq + g * G) * kHeadDim;
+
+  // Fused store: the new token sits at position L-1 of the sequence's own
+  // length, whatever the clamp to max_context_len (or to the table) left for
+  // attention.  It is written to that position's slot when the table has an
+  // entry for it (as a store through slot_mapping would), and it replaces the
+  // cached row only if attention admits that position (last < r.L).
+  const int last = FUSE ? seq_len(a, b) - 1 : -1;
+  uint4 kn = make_uint4(0, 0, 0, 0), vn = make_uint4(0, 0, 0, 0);
+  if (FUSE) {
+    const int64_t off = (static_cast<int64_t>(b) * a.num_kv_heads + g) * 16 + col;
+    kn = static_cast<const uint4*>(a.k_new)[off];
+    vn = static_cast<const uint4*>(a.v_new)[off];
+  }
+  // Head g's 256 bytes of the new K/V into the slot of position `last`.
+  // Stores share the in-order vector-memory counter with loads, so a store
+  // inside the streaming loop would make every later wait also wait for its
+  // write to be acknowledged; it is issued after the loop, where no load
+  // follows.
+  auto store_new = [&]() {
+    if (last < 0 || last / a.block_size >= a.max_blocks_per_seq) return;
+    const int lb = last / a.block_size;
+    const int blk = bt[lb];
+    if (static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks)) {
+      const int64_t off = static_cast<int64_t>(blk) * blk_stride +
+                          static_cast<int64_t>(last - lb * a.block_size) * tok_stride;
+      const_cast<uint4*>(kbase)[off] = kn;
+      const_cast<uint4*>(vbase)[off] = vn;
+    }
+  };
+  // The partition that stores (the one holding position L-1 when attention
+  // admits it, else the first; wavefront 0, the first row of lanes).
+  const bool storer = FUSE && wave == 0 && row == 0 &&
+                      pi == (last < r.L ? r.nparts - 1 : 0);
+
   if (r.nparts == 0) {
     if (pi == 0)
       for (int o = threadIdx.x; o < G * kHeadDim; o += NW * kWave) out[o] = 0;
+    if (storer) store_new();
     return;
   }
   if (pi >= r.nparts) return;
@@ -236,17 +271,6 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
   }
 #endif
 
-  // Fused store: this lane's 16 bytes of the new token's K/V row for head g.
-  // They replace what the cache holds at position L-1 when that chunk is
-  // consumed, and are written into the slot then.
-  const int last = r.L - 1;
-  uint4 kn = make_uint4(0, 0, 0, 0), vn = make_uint4(0, 0, 0, 0);
-  if (FUSE) {
-    const int64_t off = (static_cast<int64_t>(b) * a.num_kv_heads + g) * 16 + col;
-    kn = static_cast<const uint4*>(a.k_new)[off];
-    vn = static_cast<const uint4*>(a.v_new)[off];
-  }
-
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -258,10 +282,10 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
 
   // Consume one chunk held in registers (scores, online softmax, P.V).
   auto consume = [&](ChunkRegs<NL>& c, int base) {
-    if (FUSE && static_cast<unsigned>(last - base) < static_cast<unsigned>(CT)) {
+    if (FUSE && last < r.L && static_cast<unsigned>(last - base) < static_cast<unsigned>(CT)) {
       // The chunk holding the new token (a wave-uniform test): its lanes take
       // the new K/V in place of what the cache holds at that position (the
-      // slot itself is written at the end of the kernel).
+      // slot itself is written after the streaming loop).
 #pragma unroll
       for (int k = 0; k < NL; ++k) {
         if (base + 4 * k + row == last) {
@@ -354,21 +378,8 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
     }
   }
 
-  if (FUSE && wave == 0 && row == 0 && pi == r.nparts - 1) {
-    // Fused store: head g's 256 bytes of the new K/V go into the slot of
-    // position L-1 once wavefront 0 has streamed its chunks.  Stores share
-    // the in-order vector-memory counter with loads, so a store inside the
-    // streaming loop would make every later wait also wait for its write to
-    // be acknowledged; here no load follows, and the merge below hides it.
-    const int lb = last / a.block_size;   // < max_blocks_per_seq: L is capped
-    const int blk = bt[lb];
-    if (static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks)) {
-      const int64_t off = static_cast<int64_t>(blk) * blk_stride +
-                          static_cast<int64_t>(last - lb * a.block_size) * tok_stride;
-      const_cast<uint4*>(kbase)[off] = kn;
-      const_cast<uint4*>(vbase)[off] = vn;
-    }
-  }
+  // Once wavefront 0 has streamed its chunks; the merge below hides it.
+  if (storer) store_new();
   // Merge the 4 rows of the wavefront (lanes l, l^16, l^32, l^48 share a column).
 #pragma unroll
   for (int h = 0; h < G; ++h) {

@@ -11,6 +11,8 @@ checked directly:
   * prefix reuse: a prompt that starts with the full blocks of a live sequence
     reuses them (the same block ids), up to its last token;
   * eviction order: least recently freed first, a sequence's tail first;
+  * blocks filled in a step are found only after that step's commit, so no
+    batch reuses a prefix block that the same batch writes;
   * errors leave the manager unchanged.
 """
 import random
@@ -74,7 +76,11 @@ def test_fresh_allocation_and_free():
         tbl = table_of(m, 7)
         assert len(set(tbl)) == 3
         assert m.num_free_blocks == 13
+        # full blocks are pending (not findable) until the step is committed
+        assert [m.block_info(b) for b in tbl] == [(1, False)] * 3
+        assert m.commit() == 2
         assert [m.block_info(b) for b in tbl] == [(1, True), (1, True), (1, False)]
+        assert m.commit() == 0
         m.free(7)
         assert m.num_free_blocks == 16
         # freed full blocks stay registered until their space is reused
@@ -85,6 +91,7 @@ def test_prefix_reuse_shares_block_ids():
     with pk.BlockManager(32, 4) as m:
         sys_prompt = [5, 6, 7, 8, 9, 10, 11, 12]          # two full blocks
         assert m.allocate(1, sys_prompt + [1, 2, 3]) == 0
+        m.commit()
         assert m.allocate(2, sys_prompt + [4, 4, 4, 4, 4]) == 8
         t1, t2 = table_of(m, 1), table_of(m, 2)
         assert t1[:2] == t2[:2] and t1[2] != t2[2]
@@ -97,6 +104,7 @@ def test_prefix_reuse_shares_block_ids():
 def test_equal_block_after_different_prefix_is_not_shared():
     with pk.BlockManager(32, 4) as m:
         m.allocate(1, [1, 1, 1, 1, 2, 2, 2, 2, 9])
+        m.commit()
         # same second block, different first block: the chain hash differs
         assert m.allocate(2, [3, 3, 3, 3, 2, 2, 2, 2, 9]) == 0
         assert set(table_of(m, 1)).isdisjoint(table_of(m, 2))
@@ -105,8 +113,10 @@ def test_equal_block_after_different_prefix_is_not_shared():
 def test_prompt_cached_in_full_recomputes_last_block():
     with pk.BlockManager(32, 4) as m:
         m.allocate(1, list(range(8)))
+        m.commit()
         # 8 tokens, both blocks cached: the last block is recomputed
         assert m.allocate(2, list(range(8))) == 4
+        m.commit()
         t1, t2 = table_of(m, 1), table_of(m, 2)
         assert t1[0] == t2[0] and t1[1] != t2[1]
         # 9 tokens: both full blocks reused, the ninth token computed
@@ -114,12 +124,14 @@ def test_prompt_cached_in_full_recomputes_last_block():
         assert table_of(m, 3)[:2] == t1
         # a single-block prompt cached in full still computes its block
         m.allocate(4, [1, 2, 3, 4])
+        m.commit()
         assert m.allocate(5, [1, 2, 3, 4]) == 0
 
 
 def test_freed_blocks_are_reused_from_cache_and_evicted_lru():
     with pk.BlockManager(6, 4) as m:
         m.allocate(1, list(range(12)))                      # blocks a b c
+        m.commit()
         a, b, c = table_of(m, 1)
         m.free(1)                                           # freed c, b, a (tail first)
         assert m.num_free_blocks == 6
@@ -150,6 +162,9 @@ def test_append_crosses_blocks_and_registers_them():
         assert m.seq_info(1) == (5, 2, 0)
         for t in (6, 7, 8):
             m.append(1, t)
+        # the appended blocks are pending until the step is committed
+        assert m.allocate(3, [1, 2, 3, 4, 5, 6, 7, 8, 0]) == 0
+        assert m.commit() == 4                              # seq 1's two, seq 3's two
         assert m.allocate(2, [1, 2, 3, 4, 5, 6, 7, 8, 0]) == 8
         assert table_of(m, 2)[:2] == table_of(m, 1)
 
@@ -233,6 +248,7 @@ def test_random_workload_keeps_cache_semantics(seed, bs):
                 next_id += 1
             if batch:
                 write_new_tokens(m, cache, seqs, [s for s, _ in batch], [n for _, n in batch])
+            m.commit()
         elif op < 0.8:
             ids = []
             for sid in list(seqs):
@@ -245,6 +261,7 @@ def test_random_workload_keeps_cache_semantics(seed, bs):
                 seqs[sid].append(tok)
                 ids.append(sid)
             write_new_tokens(m, cache, seqs, ids, [1] * len(ids))
+            m.commit()
         else:
             sid = rnd.choice(list(seqs))
             m.free(sid)
@@ -276,8 +293,59 @@ def test_reuse_is_maximal_against_live_sequences():
                 best = max(best, n // bs * bs)
             best = min(best, (len(prompt) - 1) // bs * bs)
             assert m.allocate(sid, prompt) >= best
+            m.commit()
             live[sid] = prompt
             if rnd.random() < 0.3:
                 victim = rnd.choice(list(live))
                 m.free(victim)
                 del live[victim]
+
+
+def test_same_step_blocks_are_not_found_before_commit():
+    """A prompt's full blocks are written by the step that admits it; a second
+    prompt of the same step must not take them as its cached prefix (a fused
+    store + prefill would read them before they are written)."""
+    with pk.BlockManager(32, 4) as m:
+        sys_prompt = [5, 6, 7, 8, 9, 10, 11, 12]
+        assert m.allocate(1, sys_prompt + [1]) == 0
+        assert m.allocate(2, sys_prompt + [2]) == 0         # same step: no hit
+        t1, t2 = table_of(m, 1), table_of(m, 2)
+        assert set(t1).isdisjoint(t2)
+        # every block a batch reads as a prefix was filled before the batch
+        _, cu_q, cu_k, slots = m.prepare([1, 2], [9, 9], 8)
+        assert cu_q.tolist() == [0, 9, 18]
+        assert m.commit() == 4
+        # the next step finds them (the first copy registered under the hash)
+        assert m.allocate(3, sys_prompt + [3]) == 8
+        assert table_of(m, 3)[:2] in (t1[:2], t2[:2])
+        written = {int(s) // 4 for s in slots}
+        _, cu_q, _, slots3 = m.prepare([3], [1], 8)
+        assert set(table_of(m, 3)[:2]) <= written           # filled by the committed step
+        assert {int(s) // 4 for s in slots3}.isdisjoint(table_of(m, 3)[:2])
+
+
+def test_pending_block_freed_before_commit_is_dropped():
+    with pk.BlockManager(8, 4) as m:
+        m.allocate(1, list(range(9)))                       # two full blocks pending
+        tbl = table_of(m, 1)
+        m.free(1)
+        assert m.commit() == 0                              # nothing registered
+        assert [m.block_info(b) for b in tbl] == [(0, False)] * 3
+        assert m.allocate(2, list(range(9))) == 0           # no stale hit
+        assert m.commit() == 2
+    # a block freed and refilled before the commit is registered once, under
+    # its new content
+    with pk.BlockManager(2, 4) as m:
+        m.allocate(9, [1])                                  # holds the other block
+        m.allocate(3, [7, 7, 7, 7])
+        (b,) = table_of(m, 3)
+        m.free(3)
+        m.allocate(4, [8, 8, 8, 8])
+        assert table_of(m, 4) == [b]
+        assert m.commit() == 1
+        m.free(9)
+        assert m.allocate(5, [8, 8, 8, 8, 2]) == 4
+        assert table_of(m, 5)[0] == b
+        m.free(5)
+        m.free(4)
+        assert m.allocate(6, [7, 7, 7, 7, 2]) == 0

@@ -66,13 +66,20 @@ def assert_close(got, ref):
     assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (float(err.max()), float(err.mean()))
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["store_then_attend", "fused_store"])
 @pytest.mark.parametrize("bs", [16, 64])
-def test_block_manager_end_to_end(gpu_lib, bs):
+def test_block_manager_end_to_end(gpu_lib, bs, fused):
+    """Admissions sharing a system prompt, a free, cross-block decode steps.
+    Unfused: kv_store then paged_prefill / paged_decode.  Fused:
+    paged_prefill_store / paged_decode_store, which read prefix blocks in the
+    same launch that writes the new rows; the manager's commit rule (blocks
+    filled in a step are found only after it) keeps every prefix block they
+    read written by an earlier launch."""
     pk = gpu_lib
     rng = np.random.default_rng(2024 + bs)
     vocab = 50
-    # Exactly enough blocks for the end state, so the freed sequence's
-    # blocks (one of them registered) are evicted by the last decode steps.
+    # Exactly enough blocks (one spare at block 16) for the end state, so the
+    # freed sequence's blocks are evicted by the last decode steps.
     num_blocks = 10 if bs == 16 else 9
     mb = 16
     k_cache = torch.zeros(num_blocks, bs, HKV, D, dtype=torch.bfloat16, device="cuda")
@@ -90,26 +97,36 @@ def test_block_manager_end_to_end(gpu_lib, bs):
                 key.append(rows_for(toks[:p + 1], "k"))
                 val.append(rows_for(toks[:p + 1], "v"))
                 q.append(rows_for(toks[:p + 1], "q"))
-        pk.kv_store(bf(np.stack(key)), bf(np.stack(val)), slots.cuda(), k_cache, v_cache)
         q_ref, ref = dense_reference(seqs, ids, num_new, bs)
         assert np.array_equal(np.stack(q), q_ref)
+        kt, vt, qt = bf(np.stack(key)), bf(np.stack(val)), bf(np.stack(q))
+        if not fused:
+            pk.kv_store(kt, vt, slots.cuda(), k_cache, v_cache)
         if decode:
             ctx = (cu_k[1:] - cu_k[:-1]).cuda()
-            out = pk.paged_decode(bf(np.stack(q)), k_cache, v_cache, tables.cuda(), ctx, SCALE)
+            if fused:
+                out = pk.paged_decode_store(qt, kt, vt, k_cache, v_cache, tables.cuda(), ctx, SCALE)
+            else:
+                out = pk.paged_decode(qt, k_cache, v_cache, tables.cuda(), ctx, SCALE)
         else:
-            out = pk.paged_prefill(bf(np.stack(q)), k_cache, v_cache, tables.cuda(),
-                                   cu_q.cuda(), cu_k.cuda(), SCALE,
-                                   max_seqlen_q=int(max(num_new)))
+            args = (tables.cuda(), cu_q.cuda(), cu_k.cuda(), SCALE)
+            if fused:
+                out = pk.paged_prefill_store(qt, kt, vt, k_cache, v_cache, *args,
+                                             max_seqlen_q=int(max(num_new)))
+            else:
+                out = pk.paged_prefill(qt, k_cache, v_cache, *args, max_seqlen_q=int(max(num_new)))
+        m.commit()   # the step is enqueued: its full blocks may now be reused
         torch.cuda.synchronize()
         assert_close(out, ref)
 
-    # One prefill batch: B reuses A's system-prompt blocks (registered at once).
+    # One prefill batch: A and B share the system prompt but are admitted in
+    # the same step, so B computes it too (A's blocks are not committed yet).
     seqs[0] = system + list(rng.integers(0, vocab, bs + 3))
     seqs[1] = system + list(rng.integers(0, vocab, 5))
     new = [len(seqs[0]) - m.allocate(0, seqs[0]), len(seqs[1]) - m.allocate(1, seqs[1])]
-    assert new[0] == len(seqs[0]) and new[1] == len(seqs[1]) - 2 * bs
+    assert new[0] == len(seqs[0]) and new[1] == len(seqs[1])
     step([0, 1], new, decode=False)
-    # A finishes; C reuses the system prompt, D (no shared prefix) takes space.
+    # A finishes; C reuses the committed system prompt, D (no shared prefix) takes space.
     m.free(0)
     seqs[2] = system + list(rng.integers(0, vocab, 7))
     seqs[3] = list(rng.integers(0, vocab, bs + 1))
