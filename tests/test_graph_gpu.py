@@ -1,25 +1,40 @@
 """The library's calls under HIP graph capture: each graph is replayed several
 times with eager work and synchronisations between the replays, and every
 replay must give the eager result bit for bit (the kernels are deterministic,
-the stores idempotent).  Covers the fused decode step the bench replays, a
+the stores idempotent), and every replay's outputs are also checked against
+the CPU oracle (max-abs 2e-2, mean-abs 2e-3).  Covers the fused decode step the bench replays, a
 split-K decode (partition + combine kernels, workspace), the fused prefill
 store and the mixed batch split by kind."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads as W
 from workloads import to_torch
 
 pytestmark = pytest.mark.gpu
 
 REPLAYS = 3
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
 
 
-def replay_matches(fn, outs, keep=()):
+def close_to(ref):
+    """A check of one output tensor against an oracle result (float64)."""
+    def check(got):
+        g = got.float().cpu().numpy().astype(np.float64)
+        assert np.isfinite(g).all()
+        err = np.abs(g - ref)
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (float(err.max()), float(err.mean()))
+    return check
+
+
+def replay_matches(fn, outs, keep=(), refs=()):
     """Run fn eagerly, capture it, replay REPLAYS times; each replay's outputs
-    must equal the eager ones.  `outs` are overwritten between replays,
-    `keep` (caches the call writes) are only compared."""
+    must equal the eager ones, and refs[i] (a check against the oracle) must
+    accept outs[i] after every replay.  `outs` are overwritten between
+    replays, `keep` (caches the call writes) are only compared."""
     fn()
     torch.cuda.synchronize()
     checked = list(outs) + list(keep)
@@ -43,6 +58,8 @@ def replay_matches(fn, outs, keep=()):
         torch.cuda.synchronize()
         for o, e in zip(checked, eager):
             assert torch.equal(o.view(torch.int16), e.view(torch.int16))
+        for o, check in zip(outs, refs):
+            check(o)
 
 
 def test_graph_fused_decode_layers(gpu_lib):
@@ -63,8 +80,13 @@ def test_graph_fused_decode_layers(gpu_lib):
             pk.paged_decode_store(t["q"], t["key"], t["value"], t["k_cache"], t["v_cache"],
                                   t["block_tables"], t["context_lens"], x.scale,
                                   max_context_len=mcl, out=t["out"])
+    refs = []
+    for x, _ in layers:
+        kc, vc = oracle.kv_store(x.k_cache, x.v_cache, x.key, x.value, x.slot_mapping)
+        refs.append(close_to(oracle.paged_decode(x.q, kc, vc, x.block_tables, x.context_lens,
+                                                 x.scale)))
     replay_matches(step, [t["out"] for _, t in layers],
-                   keep=[c for _, t in layers for c in (t["k_cache"], t["v_cache"])])
+                   keep=[c for _, t in layers for c in (t["k_cache"], t["v_cache"])], refs=refs)
 
 
 def test_graph_split_decode(gpu_lib):
@@ -88,7 +110,8 @@ def test_graph_split_decode(gpu_lib):
     replay_matches(lambda: pk.paged_decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
                                            t["context_lens"], x.scale,
                                            max_context_len=int(lens.max()), out=out, workspace=ws),
-                   [out])
+                   [out], refs=[close_to(oracle.paged_decode(x.q, x.k_cache, x.v_cache, tables, lens,
+                                                             x.scale))])
 
 
 def test_graph_prefill_store_and_mixed(gpu_lib):
@@ -97,17 +120,22 @@ def test_graph_prefill_store_and_mixed(gpu_lib):
     t = to_torch(x, "cuda")
     out = torch.empty_like(t["q"])
     msq = int(np.diff(x.cu_seqlens_q).max())
+    kc, vc = oracle.kv_store(x.k_cache, x.v_cache, x.key, x.value, x.slot_mapping)
+    ref = oracle.paged_prefill(x.q, kc, vc, x.block_tables, x.cu_seqlens_q, x.cu_seqlens_k, x.scale)
     replay_matches(lambda: pk.paged_prefill_store(t["q"], t["key"], t["value"], t["k_cache"],
                                                   t["v_cache"], t["block_tables"], t["cu_seqlens_q"],
                                                   t["cu_seqlens_k"], x.scale, max_seqlen_q=msq,
                                                   out=out),
-                   [out], keep=[t["k_cache"], t["v_cache"]])
+                   [out], keep=[t["k_cache"], t["v_cache"]], refs=[close_to(ref)])
     y = W.mixed_batch()
     u = to_torch(y, "cuda")
     pk.kv_store(u["key"], u["value"], u["slot_mapping"], u["k_cache"], u["v_cache"])
     lq = np.diff(y.cu_seqlens_q)
     lk = np.diff(y.cu_seqlens_k)
     nd = int(np.sum(lq == 1))
+    kc2, vc2 = oracle.kv_store(y.k_cache, y.v_cache, y.key, y.value, y.slot_mapping)
+    ref2 = oracle.paged_prefill(y.q, kc2, vc2, y.block_tables, y.cu_seqlens_q, y.cu_seqlens_k,
+                                y.scale)
     out2 = torch.empty_like(u["q"])
     ws = torch.empty(max(pk.decode_workspace_size(nd, 16, 8, 128, int(lk[:nd].max())), 1),
                      dtype=torch.uint8, device="cuda")
@@ -116,4 +144,4 @@ def test_graph_prefill_store_and_mixed(gpu_lib):
                                                    num_decode_seqs=nd, max_seqlen_q=int(lq[nd:].max()),
                                                    max_decode_context_len=int(lk[:nd].max()),
                                                    out=out2, workspace=ws),
-                   [out2])
+                   [out2], refs=[close_to(ref2)])

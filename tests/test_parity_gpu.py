@@ -136,6 +136,24 @@ def test_long_decode_sampled(gpu_lib):
     _sampled_long(gpu_lib, 0, [0, 17, 42, 63])
 
 
+def test_long_decode_full_batch(gpu_lib):
+    """64 seqs, ctx U{4096..8192} (the split-K workload) over all 64 sequences:
+    both 1 GiB caches are copied to the host before the launch, and the oracle
+    walks the same block tables."""
+    x = W.long_decode_meta(0)
+    dev = W.long_decode_device_caches("cuda")
+    kc, vc = bits_of(dev[0]), bits_of(dev[1])
+    t = to_torch(W.PagedInputs(q=x.q, k_cache=x.q[:0], v_cache=x.q[:0],
+                               block_tables=x.block_tables, context_lens=x.context_lens,
+                               block_size=x.block_size, scale=x.scale), "cuda")
+    assert gpu_lib.decode_plan(64, 8, x.max_context_len)[1] > 1
+    out = gpu_lib.paged_decode(t["q"], dev[0], dev[1], t["block_tables"], t["context_lens"],
+                               x.scale, max_context_len=x.max_context_len)
+    torch.cuda.synchronize()
+    ref = oracle.paged_decode(x.q, kc, vc, x.block_tables, x.context_lens, x.scale)
+    assert_close(out, ref)
+
+
 def test_long_decode_window_sampled(gpu_lib):
     _sampled_long(gpu_lib, 256, [1, 5, 33, 60])
 
@@ -183,7 +201,7 @@ def _random_case(seed, lens, bs=16, hq=16, hkv=8, mb=None, window=0, scale=None)
 EDGE_LENS = [0, 1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 500, 1023, 1024]
 
 
-@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("bs", [16, 32, 48, 64, 128, 256, 512, 1024])
 @pytest.mark.parametrize("window", [0, 1, 17, 256])
 def test_decode_edge_lengths(gpu_lib, bs, window):
     x = _random_case([31, bs, window], EDGE_LENS, bs=bs, window=window)
@@ -247,9 +265,10 @@ def test_decode_block_permutation_bit_exact(gpu_lib):
     assert torch.equal(out1.view(torch.int16), out3.view(torch.int16))   # deterministic
 
 
-def test_decode_unused_table_entries_never_read(gpu_lib):
-    """Entries past ceil(L/block_size) hold a sentinel far outside the cache;
-    the result is bit-identical to a table with valid entries there."""
+def test_decode_unused_table_entries_never_used(gpu_lib):
+    """Entries past ceil(L/block_size) hold a sentinel far outside the cache
+    (the kernel may read the entry, but never uses it as a block id); the
+    result is bit-identical to a table with valid entries there."""
     x = _random_case([36], [10, 200, 64], bs=32, mb=8)
     out1 = run_decode(gpu_lib, to_torch(x, "cuda"), x)
     y = W.PagedInputs(**{**x.__dict__})
@@ -349,3 +368,36 @@ def test_decode_store_fused_deep_layer(gpu_lib):
     got, _ = _fused_vs_unfused(gpu_lib, x)
     kc, vc = oracle.kv_store(x.k_cache, x.v_cache, x.key, x.value, x.slot_mapping)
     assert_close(got, oracle_decode(x, kc, vc))
+
+
+@pytest.mark.parametrize("mcl", [80, 0])
+def test_decode_store_fused_clamped_lengths(gpu_lib, mcl):
+    """context_lens beyond max_context_len (a graph captured with a smaller
+    bound) or beyond the table row: the new row goes to position L-1 when the
+    table has an entry for it, else nowhere; attention covers the clamped
+    range.  Equal, bit for bit, to kv_store (slot -1 where no slot exists) then
+    paged_decode, and the caches change only at those slots."""
+    pk = gpu_lib
+    lens = [10, 100, 200, 64, 128, 129]
+    bs, mb = 32, 4                                   # the table covers 128 positions
+    x = _random_case([46, mcl], lens, bs=bs, mb=mb)
+    rng = np.random.default_rng([47, mcl])
+    x.key = W.normal_bf16(rng, (len(lens), 8, 128))
+    x.value = W.normal_bf16(rng, (len(lens), 8, 128))
+    x.slot_mapping = np.array([W.slot_of(x.block_tables, b, L - 1, bs) if L <= mb * bs else -1
+                               for b, L in enumerate(lens)], np.int32)
+    t1 = to_torch(x, "cuda")
+    pk.kv_store(t1["key"], t1["value"], t1["slot_mapping"], t1["k_cache"], t1["v_cache"])
+    ref = run_decode(pk, t1, x, max_context_len=mcl)
+    t2 = to_torch(x, "cuda")
+    got = pk.paged_decode_store(t2["q"], t2["key"], t2["value"], t2["k_cache"], t2["v_cache"],
+                                t2["block_tables"], t2["context_lens"], x.scale, max_context_len=mcl)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    kc, vc = oracle.kv_store(x.k_cache, x.v_cache, x.key, x.value, x.slot_mapping)
+    assert np.array_equal(bits_of(t2["k_cache"]), kc)
+    assert np.array_equal(bits_of(t2["v_cache"]), vc)
+    clamped = np.minimum(np.array(lens), min(mcl, mb * bs)).astype(np.int32)
+    ref_o = oracle.paged_decode(x.q, kc, vc, x.block_tables, clamped, x.scale)
+    assert_close(got, ref_o)
+    if mcl == 0:
+        assert not got.any()

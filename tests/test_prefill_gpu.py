@@ -82,7 +82,7 @@ SHAPES = [(0, 1), (0, 63), (0, 64), (0, 65), (100, 1), (100, 37), (5, 130), (256
           (0, 300), (513, 64)]
 
 
-@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("bs", [16, 32, 48, 64, 128, 256, 512, 1024])
 def test_prefill_shapes_block_sizes(gpu_lib, bs):
     x = prefill_case([41, bs], SHAPES, bs=bs)
     out, _ = run_store_prefill(gpu_lib, x)
