@@ -14,7 +14,6 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpagedkv.so")
-PROBE = os.path.join(HERE, "hbm_read_probe")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are kept out of generated code: ordinary float code is
@@ -56,20 +55,5 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     return LIB
 
 
-def build_probe(verbose: bool = False) -> str:
-    """The HBM read-ceiling / copy-calibration probe (a stand-alone program)."""
-    cmd = [hipcc(), "-O3", f"--offload-arch={ARCH}",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           os.path.join(HERE, "probe", "hbm_read_probe.hip"), "-o", PROBE]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {r.returncode}")
-    return PROBE
-
-
 if __name__ == "__main__":
     print(build(verbose=True))
-    print(build_probe(verbose=True))
