@@ -156,6 +156,40 @@ pk_status pk_paged_decode(void* out, const void* q,
                           void* stream);
 
 /*
+ * pk_paged_decode_noalloc — pk_paged_decode for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It allocates nothing (no hipMalloc, no hipFree, no
+ * allocating library call) and takes no workspace: the split-K partials go to
+ * a static device array of PK_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends.
+ *   - Arguments, results and errors as pk_paged_decode, without the workspace.
+ *     The output is bit-identical to pk_paged_decode's.
+ *   - A plan whose partials exceed PK_NOALLOC_SCRATCH_BYTES (what
+ *     pk_paged_decode_workspace_size reports for the same arguments) returns
+ *     PK_ERR_WORKSPACE and launches nothing; a single-partition plan needs no
+ *     scratch at all.
+ *   - The device that is current on the calling thread must be the stream's
+ *     device (PK_ERR_INVALID_ARG otherwise).  The first call on a device looks
+ *     up the array's device address (hipGetSymbolAddress); make one call per
+ *     device before capturing a graph.
+ *   - Every call on a GPU shares that GPU's array, and the array keeps the
+ *     last call's contents (nothing in it needs clearing: every partial is
+ *     written before it is read).  Calls whose kernels overlap on one GPU
+ *     (different streams without ordering between them) race on the array:
+ *     order them, e.g. issue them on one stream.
+ */
+#define PK_NOALLOC_SCRATCH_BYTES (8u << 20)
+pk_status pk_paged_decode_noalloc(void* out, const void* q,
+                                  const void* k_cache, const void* v_cache,
+                                  int32_t num_blocks, int32_t block_size,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_context_len,
+                                  float scale, int32_t sliding_window,
+                                  int32_t partition_size_request, void* stream);
+
+/*
  * pk_paged_decode_store — the decode step's store and attention in one
  * launch: for every sequence b with L_b = context_lens[b] > 0, the new token's
  * K/V rows k_new[b], v_new[b] (bf16 [num_seqs, num_kv_heads, head_dim]) are

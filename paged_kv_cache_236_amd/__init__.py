@@ -24,6 +24,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "PagedKVError", "version", "kv_store", "paged_decode", "paged_decode_store",
+    "paged_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
     "paged_prefill", "paged_prefill_store", "paged_prefill_decode",
     "decode_plan", "decode_workspace_size", "BlockManager", "check_indices",
 ]
@@ -57,6 +58,9 @@ _lib.pk_paged_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i
 _lib.pk_paged_decode.restype = ctypes.c_int
 _lib.pk_paged_decode.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p, _i32,
                                  _i32, _i32, _f32, _i32, _i32, _p, _sz, _p]
+_lib.pk_paged_decode_noalloc.restype = ctypes.c_int
+_lib.pk_paged_decode_noalloc.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p, _i32,
+                                         _i32, _i32, _f32, _i32, _i32, _p]
 _lib.pk_paged_decode_store.restype = ctypes.c_int
 _lib.pk_paged_decode_store.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p,
                                        _i32, _i32, _i32, _f32, _i32, _i32, _p, _sz, _p]
@@ -230,6 +234,40 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         _dev(block_tables, "block_tables", torch.int32, dev), int(block_tables.shape[1]),
         _dev(context_lens, "context_lens", torch.int32, dev), nseq, hq, mcl,
         float(scale), sliding_window, partition_size, ws_ptr, ws_bytes, _stream(dev)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # PK_NOALLOC_SCRATCH_BYTES in pagedkv.h
+
+
+def paged_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, *,
+                         max_context_len: int, out: torch.Tensor, sliding_window: int = 0,
+                         partition_size: int = 0) -> torch.Tensor:
+    """paged_decode for callers that cannot allocate device memory: the
+    split-K partials use the library's static per-GPU scratch
+    (NOALLOC_SCRATCH_BYTES), so neither this call nor the library allocates.
+    `out` and `max_context_len` are required (no allocation, no device sync).
+    Calls that overlap on one GPU share the scratch and race: keep them on one
+    stream."""
+    nb, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    if q.dim() != 3:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
+    nseq, hq, qd = (int(x) for x in q.shape)
+    if qd != d:
+        raise ValueError("q and cache head_dim differ")
+    if block_tables.dim() != 2 or block_tables.shape[0] != nseq or context_lens.shape != (nseq,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks] and context_lens [num_seqs]")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    dev = q.device
+    _check(_lib.pk_paged_decode_noalloc(
+        _dev(out, "out", torch.bfloat16, dev), _dev(q, "q", torch.bfloat16, dev),
+        _dev(k_cache, "k_cache", torch.bfloat16, dev), _dev(v_cache, "v_cache", torch.bfloat16, dev),
+        nb, bs, hkv, d,
+        _dev(block_tables, "block_tables", torch.int32, dev), int(block_tables.shape[1]),
+        _dev(context_lens, "context_lens", torch.int32, dev), nseq, hq, int(max_context_len),
+        float(scale), sliding_window, partition_size, _stream(dev)))
     return out
 
 

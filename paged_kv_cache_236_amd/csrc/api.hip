@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -303,6 +304,84 @@ pk_status pk_paged_decode(void* out, const void* q, const void* k_cache, const v
                            block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
                            max_context_len, scale, sliding_window, partition_size_request,
                            workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace (pk_paged_decode_noalloc): the split-K
+// partials live in `scratch`, a static device array of every GPU the library
+// runs on.  In host code `scratch` names a host-side stand-in, not the device
+// array: the device address is looked up once per device, with that device
+// current, and only that address is passed to kernels.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[PK_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device that is current and owns
+// `stream` (set-up on the first call for a device).
+pk_status scratch_address(void* stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PK_ERR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PK_ERR_UNSUPPORTED, "device %d is beyond the %d devices supported", dev, kMaxDevices);
+  if (stream) {
+    const int sdev = hipGetStreamDeviceId(static_cast<hipStream_t>(stream));
+    if (sdev != dev)
+      return fail(PK_ERR_INVALID_ARG, "the stream belongs to device %d but device %d is current",
+                  sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PK_ERR_LAUNCH, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pk_status pk_paged_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, int32_t num_blocks, int32_t block_size,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_context_len, float scale,
+                                  int32_t sliding_window, int32_t partition_size_request,
+                                  void* stream) {
+  pk_status s = check_cache_shape(num_blocks, block_size, num_kv_heads, head_dim);
+  if (s != PK_OK) return s;
+  if ((s = check_heads(num_q_heads, num_kv_heads)) != PK_OK) return s;
+  Plan p;
+  if ((s = plan_decode(num_seqs, num_kv_heads, max_context_len, sliding_window,
+                       partition_size_request, &p)) != PK_OK)
+    return s;
+  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, p);
+  if (need > PK_NOALLOC_SCRATCH_BYTES)
+    return fail(PK_ERR_WORKSPACE,
+                "pk_paged_decode_noalloc: the split-K partials need %zu bytes, more than the "
+                "%zu-byte static scratch (use pk_paged_decode with a workspace, or a larger "
+                "partition_size_request)",
+                need, static_cast<size_t>(PK_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (need > 0 && (s = scratch_address(stream, &ws)) != PK_OK) return s;
+  return paged_decode_impl(out, q, k_cache, v_cache, num_blocks, block_size, num_kv_heads, head_dim,
+                           block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                           max_context_len, scale, sliding_window, partition_size_request,
+                           ws, need > 0 ? static_cast<size_t>(PK_NOALLOC_SCRATCH_BYTES) : 0,
+                           stream, nullptr, nullptr);
 }
 
 pk_status pk_paged_decode_store(void* out, const void* q, const void* k_new, const void* v_new,

@@ -176,3 +176,22 @@ def test_check_indices_validation(lib):
     assert call(wsb=15) == WORKSPACE and "16 bytes" in msg(lib)
     assert call(ws=None) == WORKSPACE
     assert lib.pk_status_string(5) == b"PK_ERR_INDEX"
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode refuses, on the host, a plan whose partials
+    exceed its static scratch, and shape errors as pk_paged_decode does."""
+    f = lib.pk_paged_decode_noalloc
+    f.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int32] * 4 + [
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    def call(nseq=64, hq=16, mcl=8192, ps=64, d=128):
+        return f(FAKE, FAKE, FAKE, FAKE, 64, 64, 8, d, FAKE, 128, FAKE, nseq, hq, mcl, 0.088, 0,
+                 ps, None)
+    # 64 seqs x 16 heads x 128 partitions of 64 keys: 68 MB of partials > 8 MiB
+    assert call() == WORKSPACE
+    assert "static scratch" in msg(lib)
+    assert call(hq=12) == INVALID
+    assert call(ps=100) == INVALID                     # not a multiple of 64
+    assert call(d=64) == UNSUPPORTED
+    assert call(nseq=0) == OK                          # nothing to do, nothing launched
