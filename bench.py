@@ -375,7 +375,8 @@ def time_cold(fn, stream, n):
 def graph_sweep_leg(args, pk, W, dev, stream, concurrencies=(1, 8, 64), ctx=512, nl=28):
     """The 28-layer decode step (store + attend per layer, paged_decode_store)
     at c = 1, 8 and 64 sequences of context 512, eager against graph replay:
-    where launch overhead, not HBM, sets the step time at small c."""
+    where launch overhead, not HBM, sets the step time at small c.  Each mode
+    is the median of three timed runs of max(steps, 20) steps."""
     import torch
     res = {"workload": f"decode step, {nl} layers x paged_decode_store, context {ctx} "
                        "(incl. the new token), block 256, 16/8/128 bf16",
@@ -403,18 +404,23 @@ def graph_sweep_leg(args, pk, W, dev, stream, concurrencies=(1, 8, 64), ctx=512,
                 pk.paged_decode_store(q, kn, vn, kc, vc, tables, lens, 1 / math.sqrt(128),
                                       max_context_len=ctx, out=out, workspace=ws)
 
-        def timed(fn, n):
+        def timed(fn, n, reps=3):
+            # Median of `reps` timed runs of n steps each: an eager step is host-bound at
+            # small c, and a single host stall (tens of ms) would otherwise decide it.
             fn()
             torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(n):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return max(e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3) / n * 1e3
+            runs = []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(n):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                runs.append(max(e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3) / n * 1e3)
+            return sorted(runs)[len(runs) // 2]
 
         n = max(args.steps, 20)
         eager_us = timed(step, n)

@@ -16,6 +16,7 @@ library has not been built, importing this package raises ImportError.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import weakref
 from typing import Optional
@@ -120,14 +121,20 @@ def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, device=None) -> int:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
-    if device is not None and t.device != device:
+    if device is not None and t.get_device() != device.index:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device) -> int:
+    """torch's current HIP stream on `device`, as a raw handle."""
+    if _raw_stream is not None:
+        return _raw_stream(device.index)
     return torch.cuda.current_stream(device).cuda_stream
 
 
@@ -162,15 +169,28 @@ def decode_plan(num_seqs: int, num_kv_heads: int, max_context_len: int,
     return ps.value, nparts.value
 
 
+@functools.lru_cache(maxsize=1024)
+def _workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                    sliding_window, partition_size):
+    n = _lib.pk_paged_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                            max_context_len, sliding_window, partition_size)
+    if n == 0:
+        msg = _lib.pk_last_error_message().decode()
+        if msg:
+            return msg
+    return int(n)
+
+
 def decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                           max_context_len: int, sliding_window: int = 0,
                           partition_size: int = 0) -> int:
-    n = _lib.pk_paged_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                            max_context_len, sliding_window, partition_size)
-    msg = _lib.pk_last_error_message().decode()
-    if n == 0 and msg:
-        raise PagedKVError(1, msg)
-    return int(n)
+    """Workspace bytes paged_decode needs (a pure function of its arguments, so
+    the answer is cached)."""
+    n = _workspace_size(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim),
+                        int(max_context_len), int(sliding_window), int(partition_size))
+    if isinstance(n, str):
+        raise PagedKVError(1, n)
+    return n
 
 
 _workspaces = {}
