@@ -450,6 +450,13 @@ pk_status prefill_common(void* out, const void* q, const void* k_new, const void
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.sliding_window = sliding_window;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
+  {
+    // Items ranked by their key-tile count in each workgroup (longest first)
+    // when there are few enough of them; else latest query tile first.
+    const int64_t bm = 128 / a.group;
+    const int64_t items = static_cast<int64_t>(num_seqs) * ((max_seqlen_q + bm - 1) / bm);
+    a.lpt_order = items <= pk::kPrefillRankMax ? 1 : 0;
+  }
   if (capture) {   // checked and built, launched by the caller
     *capture = a;
     return ok();

@@ -77,8 +77,12 @@ struct PrefillArgs {
   int32_t max_blocks_per_seq;
   int32_t sliding_window;
   float scale_log2;
+  int32_t lpt_order;       // 1: workgroups take (sequence, query tile) items by key-tile count, most first
 };
 hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Most (sequence, query tile) items a prefill workgroup ranks by work itself.
+constexpr int kPrefillRankMax = 128;
 
 // A mixed batch in one launch: prefill work items of `p` first, then the
 // decode items of `d` (one partition per sequence).  hipErrorNotSupported

@@ -234,6 +234,92 @@ __device__ __forceinline__ u32x2_t read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
+// Work order by true work.  A query tile's cost is its number of 32-key tiles,
+// which depends on its sequence's cached prefix as well as on its index, so
+// "latest query tile first" can leave heavy tiles of long-prefix sequences to
+// the end.  Instead every workgroup ranks all (sequence, query tile) items by
+// key-tile count (most first, counts above 63 alike; ties by item index; empty
+// items last) and takes the item of rank bx / num_kv_heads, KV head
+// bx % num_kv_heads: longest processing time first.  Up to 128 items, two per
+// lane: a ballot radix select over the 6 count bits finds the count, then a
+// prefix count of the remaining candidates finds the item.  The lengths and first block-table entry of every
+// item's sequence are loaded in one round trip, and the chosen item's come
+// from the lane that loaded them.
+template <int BM>
+__device__ __forceinline__ void ranked_item(const PrefillArgs& a, int ntiles, int rank, int& b,
+                                            int& t, int& q0, int& q1, int& k0, int& k1,
+                                            int& blk0) {
+  constexpr int KPL = kPrefillRankMax / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  b = t = q0 = q1 = k0 = k1 = blk0 = 0;   // (an item is always found: the keys are distinct)
+  const int S = a.num_seqs * ntiles;
+  int vq0[KPL], vq1[KPL], vk0[KPL], vk1[KPL], vbt[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int k = min(lane + kWave * j, S - 1);
+    const int bb = k / ntiles;
+    vq0[j] = a.cu_seqlens_q[bb];
+    vq1[j] = a.cu_seqlens_q[bb + 1];
+    vk0[j] = a.cu_seqlens_k[bb];
+    vk1[j] = a.cu_seqlens_k[bb + 1];
+    vbt[j] = a.block_tables[static_cast<int64_t>(bb) * a.max_blocks_per_seq];
+  }
+  uint32_t cnt[KPL];
+  bool cand[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int k = lane + kWave * j;
+    const int tt = k % ntiles;
+    const int Lq = vq1[j] - vq0[j], Lk = vk1[j] - vk0[j], P = Lk - Lq, qa = tt * BM;
+    int n = 0;
+    if (!(Lq <= 0 || P < 0 || qa >= Lq || vq0[j] < 0 || vq0[j] + Lq > a.total_q)) {
+      const int pos_lo = P + qa, pos_hi = P + min(qa + BM, Lq) - 1;
+      const int kstart = a.sliding_window > 0 ? max(0, pos_lo - a.sliding_window + 1) : 0;
+      n = pos_hi / kBN - kstart / kBN + 1;
+    }
+    cand[j] = k < S;
+    cnt[j] = static_cast<uint32_t>(min(n, 63));
+  }
+  // The count bucket holding rank `rank`, from the top bit down: among the
+  // remaining candidates those with the bit set rank above those without.
+  int need = rank;
+#pragma unroll
+  for (int bit = 5; bit >= 0; --bit) {
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) c += __builtin_popcountll(__ballot(cand[j] && ((cnt[j] >> bit) & 1u)));
+    const bool in_ones = need < c;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const bool set = (cnt[j] >> bit) & 1u;
+      cand[j] = cand[j] && (in_ones ? set : !set);
+    }
+    need = in_ones ? need : need - c;
+  }
+  // Within the bucket, items in index order (k = lane + 64 j): the `need`-th
+  // remaining candidate, found by each candidate's count of candidates below it.
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const uint64_t m = __ballot(cand[j]);
+    const int c = __builtin_popcountll(m);
+    if (need >= 0 && need < c) {
+      const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+      const uint64_t w = __ballot(cand[j] && below == need);
+      const int src = __builtin_ctzll(w);
+      const int k = src + kWave * j;
+      b = k / ntiles;
+      t = k % ntiles;
+      q0 = __builtin_amdgcn_readlane(vq0[j], src);
+      q1 = __builtin_amdgcn_readlane(vq1[j], src);
+      k0 = __builtin_amdgcn_readlane(vk0[j], src);
+      k1 = __builtin_amdgcn_readlane(vk1[j], src);
+      blk0 = __builtin_amdgcn_readlane(vbt[j], src);
+    }
+    need -= c;
+  }
+}
+
 // POS: the softmax scale is positive, so the max of the raw scores gives the
 // max of the scaled ones and each probability is exp2(fma(s, c, -m)).
 // MODE: block addressing (kDivBlocks, kShiftBlocks or kTileInBlock).
@@ -254,22 +340,31 @@ __device__ __forceinline__ void paged_prefill_body(const PrefillArgs& a, int bx)
   const int hq = a.num_kv_heads * G;
   const float c = a.scale_log2;
 
-  // ---- work item: heaviest query tiles first ------------------------------
+  // ---- work item: most key tiles first, or latest query tiles first --------
   const int npairs = a.num_seqs * a.num_kv_heads;
   const int ntiles = (a.max_seqlen_q + BM - 1) / BM;
-  const int t = ntiles - 1 - bx / npairs;
-  const int pr = bx % npairs;
-  const int b = pr / a.num_kv_heads;
-  const int g = pr % a.num_kv_heads;
+  int t, b, g, q0, q1, k0, k1, blk_first;
+  if (a.lpt_order) {
+    g = bx % a.num_kv_heads;
+    ranked_item<BM>(a, ntiles, bx / a.num_kv_heads, b, t, q0, q1, k0, k1, blk_first);
+  } else {
+    t = ntiles - 1 - bx / npairs;
+    const int pr = bx % npairs;
+    b = pr / a.num_kv_heads;
+    g = pr % a.num_kv_heads;
+    // The sequence's lengths and its first block-table entry, fetched in one
+    // memory round trip: the empty asm needs all five values at once, so the
+    // compiler issues the five loads before a single wait (left alone it
+    // waits after each).  Without a window the first tile lies in block 0, so
+    // its DMAs need no further table lookup (the entry is judged like any
+    // other).
+    q0 = a.cu_seqlens_q[b];
+    q1 = a.cu_seqlens_q[b + 1];
+    k0 = a.cu_seqlens_k[b];
+    k1 = a.cu_seqlens_k[b + 1];
+    blk_first = a.block_tables[static_cast<int64_t>(b) * a.max_blocks_per_seq];
+  }
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
-  // The sequence's lengths and its first block-table entry, fetched in one
-  // memory round trip: the empty asm needs all five values at once, so the
-  // compiler issues the five loads before a single wait (left alone it waits
-  // after each).  Without a window the first tile lies in block 0, so its
-  // DMAs need no further table lookup (the entry is judged like any other).
-  int q0 = a.cu_seqlens_q[b], q1 = a.cu_seqlens_q[b + 1];
-  int k0 = a.cu_seqlens_k[b], k1 = a.cu_seqlens_k[b + 1];
-  int blk_first = ONE ? bt[0] : 0;
   q0 = __builtin_amdgcn_readfirstlane(q0);
   q1 = __builtin_amdgcn_readfirstlane(q1);
   k0 = __builtin_amdgcn_readfirstlane(k0);
