@@ -179,6 +179,35 @@ def test_prefill_permutation_bit_exact_and_deterministic(gpu_lib):
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
 
 
+def test_prefill_work_order_invariant(gpu_lib):
+    """Which workgroup takes which (sequence, query tile) item does not change a bit
+    of the output.  The same batch with max_seqlen_q 448 / 512 / 576 has 112 / 128
+    / 144 items: the first two are taken in order of key-tile count (ranked inside
+    the kernel, 128 being the most it ranks), the last latest query tile first.
+    Three prefixes pass 63 key tiles, where ranked counts tie; empty sequences
+    and single tokens sit between them."""
+    shapes = [(2100, 100), (2150, 90), (2300, 64), (0, 448), (0, 0), (5, 1), (256, 200),
+              (700, 0), (31, 33), (64, 64), (1000, 5), (0, 129), (512, 300), (3, 3),
+              (1500, 17), (0, 2)]
+    x = prefill_case([53], shapes, bs=256)
+    outs = []
+    t = None
+    for msq in (448, 512, 576):
+        out, t = run_store_prefill(gpu_lib, x, t=t, max_seqlen_q=msq)
+        outs.append(out.clone())
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    assert_close(outs[0], oracle_prefill(x)[0])
+    # The fused store under both orders: output and caches as store-then-prefill.
+    for msq in (512, 576):
+        out, tf = run_fused(gpu_lib, x, max_seqlen_q=msq)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), outs[0].view(torch.int16))
+        assert torch.equal(tf["k_cache"].view(torch.int16), t["k_cache"].view(torch.int16))
+        assert torch.equal(tf["v_cache"].view(torch.int16), t["v_cache"].view(torch.int16))
+
+
 def test_prefill_sentinel_padding_never_read(gpu_lib):
     x = prefill_case([49], [(10, 30), (0, 5)], bs=16, mb=8)
     out1, _ = run_store_prefill(gpu_lib, x)
