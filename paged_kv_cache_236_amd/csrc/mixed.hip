@@ -19,12 +19,14 @@ namespace {
 static_assert(kThreads == kDecodeWaves * kWave, "both kinds of workgroup have the same size");
 
 // Grid order: the prefill's heaviest `heavy` workgroups (the first half of its
-// query-tile ranks, latest tiles first), then every decode item, then the rest
-// of the prefill.  The long chains start at once; the decode rows then stream
-// on most of the GPU while those chains compute, and the short prefill items
-// fill the tail.  Measured on 48 decode rows + 4 chunks: prefill first 95.6 us,
-// the first 1 / 2 / 4 / 6 / 8 / 11 of 16 ranks first 82.2 / 81.5 / 79.8 /
-// 80.0 / 78.8 / 83.0 us, two launches 92 us.
+// work order: items ranked by key-tile count, or latest query tiles first),
+// then every decode item, then the rest of the prefill.  The long chains start
+// at once; the decode rows then stream on most of the GPU while those chains
+// compute, and the short prefill items fill the tail.  Measured on 48 decode
+// rows + 4 chunks with latest tiles first: prefill first 95.6 us, the first
+// 1 / 2 / 4 / 6 / 8 / 11 of 16 query-tile ranks first 82.2 / 81.5 / 79.8 /
+// 80.0 / 78.8 / 83.0 us, two launches 92 us; with the ranked order and the
+// first half first, 71.5 us.
 template <int G, bool POS>
 __global__ void __launch_bounds__(kThreads, 2)
 mixed_batch_kernel(PrefillArgs p, DecodeArgs d, int heavy, int decode_groups) {

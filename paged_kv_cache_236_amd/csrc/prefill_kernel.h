@@ -49,10 +49,14 @@
 // is only raised when a tile's max exceeds it by more than 2^8, so most tiles
 // skip rescaling O (probabilities stay <= 256, far inside fp32 and bf16 range).
 //
-// Work order: query tiles are issued heaviest (latest, most keys) first, and
-// with num_seqs * num_kv_heads a multiple of 8 all tiles of one (b, g) pair land
-// on the same XCD (workgroups are dealt round-robin over the 8 XCDs), so the
-// pair's K/V is reused from that XCD's L2.
+// Work order: heaviest items first.  With at most 128 (sequence, query tile)
+// items every workgroup ranks them by their number of key tiles (cached prefix
+// included) and takes the one of its rank, so the long chains start at once
+// and a sequence's query tiles run together, sharing its K/V in L2.  With more
+// items, latest query tiles (most keys of their sequence) first; then with
+// num_seqs * num_kv_heads a multiple of 8 all tiles of one (b, g) pair land on
+// the same XCD (workgroups are dealt round-robin over the 8 XCDs) and share
+// its L2.
 #pragma once
 
 #include <type_traits>
