@@ -51,7 +51,7 @@ extern "C" {
 typedef enum pk_status {
   PK_OK = 0,
   PK_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent sizes */
-  PK_ERR_UNSUPPORTED = 2,   /* a shape this build does not implement          */
+  PK_ERR_UNSUPPORTED = 2,   /* a shape the library does not implement          */
   PK_ERR_WORKSPACE = 3,     /* decode workspace missing or too small           */
   PK_ERR_LAUNCH = 4,        /* the HIP runtime rejected a kernel launch        */
   PK_ERR_INDEX = 5          /* checked mode: index arrays violate a contract   */
