@@ -288,7 +288,7 @@ def main():
         "attn_tokens_per_s": round(64 / (ms_per_step * 1e-3), 1),
         "eager_ms_per_step": round(max(eager_ms, eager_wall_ms), 4),
         "roofline": {
-            "kernel": ("decode_partition_kernel" + ("" if nparts == 1 else " + decode_combine_kernel")
+            "kernel": (("decode_partition_kernel" if nparts == 1 else "decode_partition_merged_kernel")
                        + ("" if args.unfused else " (fused store)")),
             "bound": "hbm",
             "achieved": round(dec_gbs, 1),

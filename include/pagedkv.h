@@ -1,7 +1,8 @@
 /*
  * pagedkv.h — C ABI of a gfx950 (MI355X) library for attention over a paged
  * KV cache: storing new K/V into cache blocks, decode attention (one query
- * token per sequence, split-K with a combine pass, optional sliding window)
+ * token per sequence, split-K with the partials merged in the same launch,
+ * optional sliding window)
  * and variable-length causal prefill over a partly cached prefix.
  *
  * Sources.  nano-vllm-rs README, "Run Inference" (the KV-cache block size is a
@@ -90,10 +91,20 @@ pk_status pk_kv_store(const void* key, const void* value,
  * partitions of `partition_size` tokens (a multiple of 64) starting at its
  * first admitted key (with a sliding window W: ceil(min(L, W) / partition_size)
  * partitions); each partition is
- * reduced by one workgroup to a partial softmax state, and a combine kernel
- * merges the partials (split-K / flash-decoding).  When every sequence fits
- * one partition the combine pass is skipped and the partition kernel writes
- * the output directly.
+ * reduced by one workgroup to a partial softmax state, and the partials are
+ * merged (split-K / flash-decoding).  The merge happens in the same launch:
+ * each (sequence, KV head) counts its finished partitions on a device-scope
+ * counter, and the partition that finishes last merges them.  The counters
+ * come from a pool of 2^20 that the library holds on every GPU it runs on
+ * (zero when the library loads; every merge leaves its counter at zero); each
+ * split call takes num_seqs * num_kv_heads of them in turn, so calls in flight
+ * together use distinct counters unless more than 2^20 (sequence, KV head)
+ * pairs are in flight at once.  The first split call on a device looks up the
+ * pool's device address (hipGetSymbolAddress): make one call per device before
+ * capturing a graph.  When the stream's device is not the current one, or a
+ * call has more pairs than the pool, a second (combine) launch merges instead,
+ * with the same arithmetic.  When every sequence fits one partition the
+ * partition kernel writes the output directly.
  *
  * pk_paged_decode_plan: the partition size and the number of partition slots
  * per sequence that pk_paged_decode will use for these arguments.

@@ -142,6 +142,50 @@ size_t workspace_bytes_for(int32_t num_seqs, int32_t num_q_heads, const Plan& p)
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Merge counters for split decode, one per (sequence, KV head) of a call: a
+// static pool on every GPU the library runs on, zero when the module loads;
+// the partition that merges a pair sets its counter back to zero.  Each call
+// takes the next num_seqs * num_kv_heads counters of its device's pool,
+// wrapping at the end, so calls in flight at the same time use different
+// counters unless more than kMergeCounters pairs are in flight together.  In
+// host code `merge_counters` names a host-side stand-in: the device address is
+// looked up once per device, with that device current.
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int64_t kMergeCounters = int64_t{1} << 20;
+static __device__ __align__(256) int32_t merge_counters[kMergeCounters];
+std::mutex g_counter_mu;
+int32_t* g_counter_ptr[kMaxDevices] = {};
+int64_t g_counter_next[kMaxDevices] = {};
+
+// Counters for `pairs` pairs on the device that runs `stream`, or nullptr when
+// none can be had (the stream's device is not the current one, the lookup
+// failed, or the call has more pairs than the pool): a combine launch then
+// merges the partitions.
+int32_t* take_merge_counters(void* stream, int64_t pairs) {
+  if (pairs <= 0 || pairs > kMergeCounters) return nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (stream && hipGetStreamDeviceId(static_cast<hipStream_t>(stream)) != dev) return nullptr;
+  std::lock_guard<std::mutex> lock(g_counter_mu);
+  if (!g_counter_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(merge_counters)) != hipSuccess || !p) {
+      (void)hipGetLastError();   // leave no error for the launch check to find
+      return nullptr;
+    }
+    g_counter_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  if (g_counter_next[dev] + pairs > kMergeCounters) g_counter_next[dev] = 0;
+  int32_t* t = g_counter_ptr[dev] + g_counter_next[dev];
+  g_counter_next[dev] += pairs;
+  return t;
+}
+
+}  // namespace
+
 static pk_status paged_decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                           int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                           int32_t head_dim, const int32_t* block_tables,
@@ -205,6 +249,9 @@ static pk_status paged_decode_impl(void* out, const void* q, const void* k_cache
   // sequences of 4096-8192 keys with a 256-key window).
   a.length_order = p.num_parts == 1 && num_seqs <= kOrderMaxSeqs &&
                    num_seqs * num_kv_heads > kNumCUs && sliding_window == 0;
+  a.merge_counters = p.num_parts > 1
+                         ? take_merge_counters(stream, static_cast<int64_t>(num_seqs) * num_kv_heads)
+                         : nullptr;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
   a.cu_seqlens_q = cu_seqlens_q;
   a.cu_seqlens_k = cu_seqlens_k;
@@ -318,7 +365,6 @@ namespace {
 
 static __device__ __align__(256) unsigned char scratch[PK_NOALLOC_SCRATCH_BYTES];
 
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 

@@ -1,7 +1,8 @@
 // paged_decode: attention of one query token per sequence over the paged KV
 // cache (nano-vllm-sansho README, "Sansho Serving Roofline Anchors": the q=1
 // decode step, and its sliding-window-256 model), split over the context
-// (flash-decoding) with a separate combine kernel.
+// (flash-decoding), the partitions merged in the same launch by the last of
+// them to finish (or by a separate combine kernel).
 //
 // Work decomposition.  For (sequence b, KV head g) the admitted key positions
 // [lo, L) are cut into partitions of PS tokens starting at lo.
@@ -23,8 +24,11 @@
 // fp32 and the hardware exp2 is used.
 //
 // A partition's result is either written as the final bf16 output (when the
-// sequence has a single partition) or as the partial state (m, l, acc) that
-// the combine kernel merges: out = sum_p 2^(m_p-M) acc_p / sum_p 2^(m_p-M) l_p.
+// sequence has a single partition) or as the partial state (m, l, acc) that is
+// merged: out = sum_p 2^(m_p-M) acc_p / sum_p 2^(m_p-M) l_p.  The merge is done
+// by the sequence's last partition to finish (a device-scope arrival counter),
+// or, without counters, by the combine kernel; both use the same code, so the
+// results are bit-identical.
 #pragma once
 
 #include "device_common.h"
@@ -172,7 +176,38 @@ __device__ __forceinline__ void length_ordered_item(const DecodeArgs& a, int by,
 
 // One workgroup's work; (bx, by, bz) = (partition, KV head, sequence) in the
 // kernel's own grid.  Also run by the mixed-batch kernel (mixed.hip).
-template <int G, int NW, int NL, bool FUSE>
+// The output of (query head `head`, dim d) from the partials of its `nparts`
+// partitions: one online pass in partition order, out = sum_p 2^(m_p-M) acc_p /
+// sum_p 2^(m_p-M) l_p.  Each step's loads do not depend on the running state,
+// so the unrolled loads are all in flight together.  COH: device-coherent loads
+// (partials written by workgroups of the same launch).
+template <bool COH>
+__device__ __forceinline__ float merge_partials(const DecodeArgs& a, int64_t head, int d, int nparts) {
+  const float* ml = a.ws_ml + head * a.num_parts * 2;
+  const float* acc = a.ws_acc + head * a.num_parts * kHeadDim + d;
+  auto ld = [](const float* p) __attribute__((always_inline)) {
+    if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+  };
+  float mx = kEmptyMax, ls = 0.f, av = 0.f;
+#pragma unroll 4
+  for (int p = 0; p < nparts; ++p) {
+    const float mp = ld(ml + 2 * p);
+    const float lp = ld(ml + 2 * p + 1);
+    const float ap = ld(acc + p * kHeadDim);
+    const float mn = fmaxf(mx, mp);
+    const float fo = fast_exp2(mx - mn);
+    const float fn = fast_exp2(mp - mn);
+    ls = ls * fo + lp * fn;
+    av = av * fo + ap * fn;
+    mx = mn;
+  }
+  return ls > 0.f ? av / ls : 0.f;
+}
+
+// MERGE: a split sequence's partitions are merged in the same launch by the
+// last of them to finish (a.merge_counters); else by the combine kernel.
+template <int G, int NW, int NL, bool FUSE, bool MERGE = false>
 __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int bx, int by, int bz) {
   constexpr int CT = 4 * NL;   // tokens per chunk
   const int lane = threadIdx.x & (kWave - 1);
@@ -435,13 +470,51 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
       out[o] = static_cast<uint16_t>(f32_to_bf16_bits(ls > 0.f ? av / ls : 0.f));
     } else {
       const int64_t slot = (static_cast<int64_t>(b) * hq + g * G + h) * a.num_parts + pi;
-      a.ws_acc[slot * kHeadDim + d] = av;
-      if (d == 0) {
-        a.ws_ml[slot * 2] = mx;
-        a.ws_ml[slot * 2 + 1] = ls;
+      if constexpr (MERGE) {
+        // Device-coherent stores: the merging workgroup may run on another XCD,
+        // whose L2 does not see this one's.
+        __hip_atomic_store(a.ws_acc + slot * kHeadDim + d, av, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) {
+          __hip_atomic_store(a.ws_ml + slot * 2, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(a.ws_ml + slot * 2 + 1, ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else {
+        a.ws_acc[slot * kHeadDim + d] = av;
+        if (d == 0) {
+          a.ws_ml[slot * 2] = mx;
+          a.ws_ml[slot * 2 + 1] = ls;
+        }
       }
     }
-  }}
+  }
+  if constexpr (MERGE) {
+    if (r.nparts > 1) {
+      // Once this workgroup's partial stores are complete (every wavefront
+      // waits for its own, then the barrier), one arrival on the pair's
+      // counter.  The partition that brings it to nparts merges all of them
+      // and sets the counter back to zero; the others are done.  No workgroup
+      // waits for another.  Device-coherent stores completed before the
+      // arrival and device-coherent loads after it make the partials visible
+      // without cache write-backs or invalidations.
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wavefront's stores acknowledged
+      __syncthreads();
+      __shared__ int s_merge;
+      if (threadIdx.x == 0) {
+        int32_t* t = a.merge_counters + static_cast<int64_t>(b) * a.num_kv_heads + g;
+        const int arrived = __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = arrived == r.nparts - 1;
+        if (last) __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_merge = last;
+      }
+      __syncthreads();
+      if (!s_merge) return;
+      for (int o = threadIdx.x; o < G * kHeadDim; o += NW * kWave) {
+        const int64_t head = static_cast<int64_t>(b) * hq + g * G + o / kHeadDim;
+        out[o] = static_cast<uint16_t>(f32_to_bf16_bits(merge_partials<true>(a, head, o % kHeadDim, r.nparts)));
+      }
+    }
+  }
+}
 
 template <int G, int NW, int NL, bool FUSE>
 __global__ void __launch_bounds__(NW * kWave)
@@ -449,7 +522,19 @@ decode_partition_kernel(DecodeArgs a) {
   decode_partition_body<G, NW, NL, FUSE>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-// Merge the partitions of every sequence that has more than one.
+// Split plans with the merge in the same launch: a 1D grid, partition fastest,
+// then KV head, then sequence (the decode kernel's grid order, flattened).
+template <int G, int NW, int NL, bool FUSE>
+__global__ void __launch_bounds__(NW * kWave)
+decode_partition_merged_kernel(DecodeArgs a) {
+  const int w = static_cast<int>(blockIdx.x);
+  const int pi = w % a.num_parts;
+  const int pair = w / a.num_parts;
+  decode_partition_body<G, NW, NL, FUSE, true>(a, pi, pair % a.num_kv_heads, pair / a.num_kv_heads);
+}
+
+// Merge the partitions of every sequence that has more than one (split plans
+// without merge counters).
 template <int G>
 __global__ void __launch_bounds__(G * kHeadDim)
 decode_combine_kernel(DecodeArgs a) {
@@ -461,25 +546,8 @@ decode_combine_kernel(DecodeArgs a) {
   const int h = threadIdx.x / kHeadDim;
   const int d = threadIdx.x % kHeadDim;
   const int64_t head = static_cast<int64_t>(b) * hq + g * G + h;
-  const float* ml = a.ws_ml + head * a.num_parts * 2;
-  const float* acc = a.ws_acc + head * a.num_parts * kHeadDim + d;
-  // One online pass; each step's loads do not depend on the running state,
-  // so the unrolled loads are all in flight together.
-  float mx = kEmptyMax, ls = 0.f, av = 0.f;
-#pragma unroll 4
-  for (int p = 0; p < r.nparts; ++p) {
-    const float mp = ml[2 * p];
-    const float lp = ml[2 * p + 1];
-    const float ap = acc[p * kHeadDim];
-    const float mn = fmaxf(mx, mp);
-    const float fo = fast_exp2(mx - mn);
-    const float fn = fast_exp2(mp - mn);
-    ls = ls * fo + lp * fn;
-    av = av * fo + ap * fn;
-    mx = mn;
-  }
   static_cast<uint16_t*>(a.out)[(static_cast<int64_t>(r.row) * hq + g * G + h) * kHeadDim + d] =
-      static_cast<uint16_t>(f32_to_bf16_bits(ls > 0.f ? av / ls : 0.f));
+      static_cast<uint16_t>(f32_to_bf16_bits(merge_partials<false>(a, head, d, r.nparts)));
 }
 
 constexpr int kDecodeWaves = PK_DECODE_WAVES;

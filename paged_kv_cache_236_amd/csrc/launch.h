@@ -45,6 +45,8 @@ struct DecodeArgs {
   int32_t partition_size;
   int32_t num_parts;       // partition slots per sequence
   int32_t length_order;    // 1: workgroups take (seq, head) items longest-first, paired long/short
+  int32_t* merge_counters; // split plans: one arrival counter per (seq, KV head), zero between
+                           // launches; nullptr: a combine launch merges the partitions
   float scale_log2;        // softmax scale * log2(e)
   // Varlen form (decode rows of a mixed batch), or nullptr: sequence b's
   // length is cu_seqlens_k[b+1] - cu_seqlens_k[b] (context_lens unused) and its

@@ -3,7 +3,7 @@ times with eager work and synchronisations between the replays, and every
 replay must give the eager result bit for bit (the kernels are deterministic,
 the stores idempotent), and every replay's outputs are also checked against
 the CPU oracle (max-abs 2e-2, mean-abs 2e-3).  Covers the fused decode step the bench replays, a
-split-K decode (partition + combine kernels, workspace), the fused prefill
+split-K decode (partitions merged in the same launch, workspace), the fused prefill
 store and the mixed batch split by kind."""
 import numpy as np
 import pytest
@@ -90,8 +90,9 @@ def test_graph_fused_decode_layers(gpu_lib):
 
 
 def test_graph_split_decode(gpu_lib):
-    """Few long sequences: split into partitions, merged by the combine kernel
-    through the workspace."""
+    """Few long sequences: split into partitions whose partials (in the
+    workspace) are merged in the same launch through the merge counters, which
+    every replay reuses."""
     pk = gpu_lib
     rng = np.random.default_rng(71)
     lens = np.array([4000, 2500, 3100, 17], np.int32)

@@ -355,7 +355,7 @@ def test_mixed_split_workload(gpu_lib):
 @pytest.mark.parametrize("window", [0, 100])
 def test_mixed_split_extremes_and_long(gpu_lib, window):
     """All prefill, all decode, and decode contexts long enough to be split
-    over partitions (combine kernel, workspace) next to prefill chunks."""
+    over partitions (merged in their own launch, workspace) next to prefill chunks."""
     shapes = [(5000, 1), (1, 1), (3000, 1), (700, 1), (0, 90), (300, 33)]
     x = prefill_case([55, window], shapes, bs=64, window=window)
     for nd in (0, 4):
