@@ -97,11 +97,15 @@ pk_status pk_kv_store(const void* key, const void* value,
  * counter, and the partition that finishes last merges them.  The counters
  * come from a pool of 2^20 that the library holds on every GPU it runs on
  * (zero when the library loads; every merge leaves its counter at zero); each
- * split call takes num_seqs * num_kv_heads of them in turn, so calls in flight
- * together use distinct counters unless more than 2^20 (sequence, KV head)
- * pairs are in flight at once.  The first split call on a device looks up the
- * pool's device address (hipGetSymbolAddress): make one call per device before
- * capturing a graph.  When the stream's device is not the current one, or a
+ * split call takes the next num_seqs * num_kv_heads of them when it is made
+ * (wrapping at the end of the pool; a call captured into a graph keeps its
+ * counters for every replay).  Two launches that may run at the same time on
+ * one GPU therefore use distinct counters unless 2^20 or more pairs' worth of
+ * split calls were made between them, e.g. a graph replayed on one stream
+ * while that many calls went through another.  The first split call on a
+ * device looks up the pool's device address (hipGetSymbolAddress): make one
+ * call per device before capturing a graph.  When the stream's device is not
+ * the current one, or a
  * call has more pairs than the pool, a second (combine) launch merges instead,
  * with the same arithmetic.  When every sequence fits one partition the
  * partition kernel writes the output directly.
