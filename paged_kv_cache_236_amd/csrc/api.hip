@@ -109,20 +109,26 @@ pk_status plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max_contex
     const int64_t pairs = static_cast<int64_t>(std::max(num_seqs, 1)) * num_kv_heads;
     if (pairs >= kNumCUs) {
       // The grid already covers every CU: one partition per pair up to 2048
-      // keys (no combine launch), 2048-key partitions beyond.
+      // keys (no merge; splitting the c = 64 layer in two: 43.8 against
+      // 35.6 us), 2048-key partitions beyond.
       ps = 64;
       const int64_t want = std::min<int64_t>(eff, 2048);
       while (ps < want) ps *= 2;
     } else if (eff <= kNoSplitKeys) {
       // Few pairs and short contexts: the whole batch is a few microseconds of
-      // latency, and a combine launch would cost more than splitting saves
-      // (8 sequences of <= 128 keys: 5.0 us in one partition, 7.1 us split).
+      // latency, and the merge costs more than splitting saves (8 sequences of
+      // <= 128 keys: 5.2 us in one partition, 6.6 us in two).
       ps = 64;
       while (ps < eff) ps *= 2;
     } else {
-      // Few pairs: split until >= 2 workgroups per CU, 64 keys at least.
+      // Few pairs: split until the grid has a workgroup per CU, 64 keys at
+      // least.  Larger partitions on fewer CUs beat more, smaller ones (each
+      // split partition pays its merge arrival): c = 8 at 512 keys 7.9 us in
+      // 128-key partitions against 9.3 us in 64-key ones, c = 2 at 4096 keys
+      // 12.4 against 15.9 us, c = 4 at 1024 keys 8.4 against 11.6 us; one
+      // workgroup per two CUs is slower again (c = 8 at 512 keys: 9.5 us).
       ps = 2048;
-      while (ps > kPartitionQuantum && pairs * slots_for(ctx, sliding_window, ps) < 2 * kNumCUs) ps /= 2;
+      while (ps > kPartitionQuantum && pairs * slots_for(ctx, sliding_window, ps) < kNumCUs) ps /= 2;
     }
   }
   const int64_t slots = slots_for(ctx, sliding_window, ps);
