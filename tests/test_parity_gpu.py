@@ -137,21 +137,24 @@ def test_long_decode_sampled(gpu_lib):
 
 
 def test_long_decode_full_batch(gpu_lib):
-    """64 seqs, ctx U{4096..8192} (the split-K workload) over all 64 sequences:
-    both 1 GiB caches are copied to the host before the launch, and the oracle
-    walks the same block tables."""
+    """64 seqs, ctx U{4096..8192} over all 64 sequences, in the planner's plan
+    (one partition per sequence, longest first) and split into 2048-key
+    partitions merged in the same launch: both 1 GiB caches are copied to the
+    host before the launches, and the oracle walks the same block tables."""
     x = W.long_decode_meta(0)
     dev = W.long_decode_device_caches("cuda")
     kc, vc = bits_of(dev[0]), bits_of(dev[1])
     t = to_torch(W.PagedInputs(q=x.q, k_cache=x.q[:0], v_cache=x.q[:0],
                                block_tables=x.block_tables, context_lens=x.context_lens,
                                block_size=x.block_size, scale=x.scale), "cuda")
-    assert gpu_lib.decode_plan(64, 8, x.max_context_len)[1] > 1
-    out = gpu_lib.paged_decode(t["q"], dev[0], dev[1], t["block_tables"], t["context_lens"],
-                               x.scale, max_context_len=x.max_context_len)
-    torch.cuda.synchronize()
     ref = oracle.paged_decode(x.q, kc, vc, x.block_tables, x.context_lens, x.scale)
-    assert_close(out, ref)
+    assert gpu_lib.decode_plan(64, 8, x.max_context_len)[1] == 1
+    assert gpu_lib.decode_plan(64, 8, x.max_context_len, 0, 2048)[1] == 4
+    for ps in (0, 2048):
+        out = gpu_lib.paged_decode(t["q"], dev[0], dev[1], t["block_tables"], t["context_lens"],
+                                   x.scale, max_context_len=x.max_context_len, partition_size=ps)
+        torch.cuda.synchronize()
+        assert_close(out, ref)
 
 
 def test_long_decode_window_sampled(gpu_lib):
