@@ -113,7 +113,8 @@ pk_status pk_kv_store(const void* key, const void* value,
  * pk_paged_decode_plan: the partition size and the number of partition slots
  * per sequence that pk_paged_decode will use for these arguments.
  * `partition_size_request` 0 asks for the built-in choice; otherwise it must
- * be a positive multiple of 64.
+ * be a positive multiple of 64, at most 2^30 (PK_ERR_INVALID_ARG otherwise).
+ * The built-in choice is a power of two from 64 to 2^30.
  */
 pk_status pk_paged_decode_plan(int32_t num_seqs, int32_t num_kv_heads,
                                int32_t max_context_len, int32_t sliding_window,
@@ -145,7 +146,10 @@ size_t pk_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *   context_lens  int32 [num_seqs]; L_b keys, including the new token, which
  *                 is the query (it must already be stored, e.g. by
  *                 pk_kv_store earlier on the same stream).  Values are clamped
- *                 to [0, max_blocks_per_seq * block_size].
+ *                 to [0, max_blocks_per_seq * block_size]; a table row may
+ *                 address at most 2^31 - 1 tokens (PK_ERR_UNSUPPORTED
+ *                 otherwise).
+ *   num_seqs      at most 65535 per call (PK_ERR_UNSUPPORTED otherwise)
  *   max_context_len  host-side upper bound of context_lens, used to plan the
  *                 split; keys of a sequence beyond it are not attended.
  *   scale         softmax scale applied to q.k (1/sqrt(head_dim) usually)

@@ -44,6 +44,9 @@ constexpr int64_t kPartitionQuantum = 64;   // 4 wavefronts x 16-token chunks
 constexpr int64_t kNumCUs = 256;            // MI355X: 8 XCDs x 32 CUs
 constexpr int32_t kOrderMaxSeqs = 64;       // sequences one wavefront can rank
 constexpr int64_t kNoSplitKeys = 256;       // with few pairs, contexts this short are not split
+constexpr int64_t kMaxPartition = int64_t{1} << 30;   // partition sizes stay far inside int32
+constexpr int64_t kMaxSlots = 65535;         // partition slots per sequence
+constexpr int32_t kMaxDecodeSeqs = 65535;    // sequences per decode call (a grid dimension)
 
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
@@ -80,11 +83,9 @@ struct Plan {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Partition slots a sequence can touch: ceil(L/PS) without a window; a window
-// of W keys starting anywhere inside a partition spans at most
-// (W + PS - 2) / PS + 1 partitions.
+// Partition slots one sequence needs: partitions start at its first admitted
+// key, so its min(L, W) admitted keys (L without a window) take ceil(./PS).
 int64_t slots_for(int64_t max_ctx, int64_t window, int64_t ps) {
-  // Partitions start at each sequence's first admitted key.
   const int64_t keys = window > 0 ? std::min(max_ctx, window) : max_ctx;
   const int64_t n = ceil_div(keys, ps);
   return std::max<int64_t>(n, 1);
@@ -98,9 +99,9 @@ pk_status plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max_contex
     return fail(PK_ERR_INVALID_ARG, "max_context_len must be >= 0 (got %d)", max_context_len);
   if (sliding_window < 0)
     return fail(PK_ERR_INVALID_ARG, "sliding_window must be >= 0 (got %d)", sliding_window);
-  if (request < 0 || request % kPartitionQuantum != 0)
-    return fail(PK_ERR_INVALID_ARG, "partition_size_request %d must be 0 or a positive multiple of 64",
-                request);
+  if (request < 0 || request % kPartitionQuantum != 0 || request > kMaxPartition)
+    return fail(PK_ERR_INVALID_ARG,
+                "partition_size_request %d must be 0 or a positive multiple of 64 up to 2^30", request);
   const int64_t ctx = std::max<int32_t>(max_context_len, 1);
   int64_t ps = request;
   if (ps == 0) {
@@ -114,7 +115,7 @@ pk_status plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max_contex
       // against 35.6 us; 64 sequences of 4096..8192 keys in 2048-key
       // partitions 286 against 245 us.
       ps = 64;
-      while (ps < eff) ps *= 2;
+      while (ps < eff && ps < kMaxPartition) ps *= 2;
     } else if (eff <= kNoSplitKeys) {
       // Few pairs and short contexts: the whole batch is a few microseconds of
       // latency, and the merge costs more than splitting saves (8 sequences of
@@ -130,10 +131,12 @@ pk_status plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max_contex
       // workgroup per two CUs is slower again (c = 8 at 512 keys: 9.5 us).
       ps = 2048;
       while (ps > kPartitionQuantum && pairs * slots_for(ctx, sliding_window, ps) < kNumCUs) ps /= 2;
+      // Beyond kMaxSlots partitions of 2048 keys: larger partitions.
+      while (slots_for(ctx, sliding_window, ps) > kMaxSlots && ps < kMaxPartition) ps *= 2;
     }
   }
   const int64_t slots = slots_for(ctx, sliding_window, ps);
-  if (slots > 65535) return fail(PK_ERR_UNSUPPORTED, "too many partitions (%lld)", (long long)slots);
+  if (slots > kMaxSlots) return fail(PK_ERR_UNSUPPORTED, "too many partitions (%lld)", (long long)slots);
   plan->partition_size = static_cast<int32_t>(ps);
   plan->num_parts = static_cast<int32_t>(slots);
   return PK_OK;
@@ -209,6 +212,13 @@ static pk_status paged_decode_impl(void* out, const void* q, const void* k_cache
   if ((s = check_heads(num_q_heads, num_kv_heads)) != PK_OK) return s;
   if (max_blocks_per_seq <= 0)
     return fail(PK_ERR_INVALID_ARG, "max_blocks_per_seq must be > 0 (got %d)", max_blocks_per_seq);
+  if (num_seqs > kMaxDecodeSeqs)
+    return fail(PK_ERR_UNSUPPORTED, "at most %d sequences per decode call (got %d)", kMaxDecodeSeqs,
+                num_seqs);
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX)
+    return fail(PK_ERR_UNSUPPORTED,
+                "max_blocks_per_seq * block_size = %lld tokens per table row exceeds 2^31 - 1",
+                static_cast<long long>(max_blocks_per_seq) * block_size);
   if (!std::isfinite(scale)) return fail(PK_ERR_INVALID_ARG, "scale must be finite");
   Plan p;
   if ((s = plan_decode(num_seqs, num_kv_heads, max_context_len, sliding_window,

@@ -79,7 +79,8 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeArgs& a, int b) {
   r.lo = a.sliding_window > 0 ? max(0, r.L - a.sliding_window) : 0;
   // Partitions start at lo (not at multiples of the partition size), so a
   // window of W keys takes ceil(W / partition_size) of them.
-  r.nparts = r.L > 0 ? (r.L - r.lo + a.partition_size - 1) / a.partition_size : 0;
+  const int keys = r.L - r.lo;   // written so that nothing below can overflow int32
+  r.nparts = r.L > 0 ? keys / a.partition_size + (keys % a.partition_size != 0) : 0;
   // The host plan sizes num_parts for the worst sequence; the clamp only keeps
   // workspace indexing in bounds should a caller break that contract.
   r.nparts = min(r.nparts, a.num_parts);
@@ -283,7 +284,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
   }
   if (pi >= r.nparts) return;
   const int t0 = r.lo + pi * a.partition_size;
-  const int t1 = min(t0 + a.partition_size, r.L);
+  const int t1 = t0 + min(a.partition_size, r.L - t0);
 
 #if PK_DECODE_DOT2
   // q kept as packed bf16 pairs; the scale is applied to the reduced score.

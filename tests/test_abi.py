@@ -86,6 +86,9 @@ def decode(lib, **kw):
     (dict(maxctx=-5), INVALID, "max_context_len"),
     (dict(win=-1), INVALID, "sliding_window"),
     (dict(ps=100), INVALID, "partition_size"),
+    (dict(ps=(1 << 30) + 64), INVALID, "2^30"),
+    (dict(mb=(1 << 21) + 1, bs=1024), UNSUPPORTED, "2^31 - 1"),
+    (dict(nseq=65536), UNSUPPORTED, "sequences per decode call"),
     (dict(scale=float("nan")), INVALID, "scale"),
     (dict(q=None), INVALID, "null"),
     (dict(bt=None), INVALID, "null"),
