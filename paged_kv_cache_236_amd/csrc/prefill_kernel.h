@@ -630,13 +630,13 @@ __device__ __forceinline__ void paged_prefill_body(const PrefillArgs& a, int bx)
     }
 
     // Issue priority: two workgroups share each SIMD, one wavefront each.  A
-    // wavefront drops to the lower priority while it issues its operand reads
+    // wavefront takes the lowest priority while it issues its operand reads
     // and S products (a dependent chain of matrix products with idle issue
-    // slots between them) and takes the higher one from its softmax on, so
-    // the other wavefront's softmax, P.V and ring bookkeeping go first and
-    // the S products fill the gaps.  Prefix workload 33.2-33.3 against
-    // 34.3 us, mixed batch split by kind 71.2 against 72.7-73.2 us; the fused
-    // store and short items unchanged.
+    // slots between them), the highest for its softmax (the serial part of
+    // the tile), a middle one for P.V, the ring bookkeeping and the next
+    // barrier, and the highest again for the epilogue.  The S products then
+    // fill the gaps of the other wavefront's softmax.  Prefix workload 32.1
+    // against 34.3 us with no priority changes.
     __builtin_amdgcn_s_setprio(0);
 
     // ---- operand reads (compiler-visible: it waits for each just before its
@@ -670,7 +670,7 @@ __device__ __forceinline__ void paged_prefill_body(const PrefillArgs& a, int bx)
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
 
-    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(2);
 
     // ---- online softmax over this lane's column ------------------------------
     // (16 keys of the tile in this lane, the other 16 in lane ^ 32)
@@ -711,6 +711,8 @@ __device__ __forceinline__ void paged_prefill_body(const PrefillArgs& a, int bx)
         for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
     }
 
+    __builtin_amdgcn_s_setprio(1);
+
     // ---- O^T += V^T . P^T ------------------------------------------------------
     // In step ks2 the lane's 8 key slots are keys 16*ks2 + 4*hgrp + {0..3} and
     // 16*ks2 + 8 + 4*hgrp + {0..3} of the tile: accumulator registers
@@ -749,6 +751,7 @@ __device__ __forceinline__ void paged_prefill_body(const PrefillArgs& a, int bx)
     step(kt, std::integral_constant<int, 3>{});
     if (++kt > tile1) break;
   }
+  __builtin_amdgcn_s_setprio(2);
   // Drain this wave's remaining (clamped, unused) DMAs before the wave ends.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
