@@ -105,6 +105,23 @@ __device__ __forceinline__ uint4 load16(const uint4* p) {
 #endif
 }
 
+// The chunk at token `base`, whose cache block (logical block lb of the
+// sequence) has table entry blk.
+template <int NL>
+__device__ __forceinline__ void load_chunk_at(ChunkRegs<NL>& c, const DecodeArgs& a, int blk, int lb,
+                                              bool dummy, const uint4* kbase, const uint4* vbase,
+                                              int64_t tok_stride, int64_t blk_stride, int base) {
+  c.ok = !dummy && static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
+  blk = c.ok ? blk : 0;
+  c.off = dummy ? 0
+                : static_cast<int64_t>(blk) * blk_stride +
+                      static_cast<int64_t>(base - lb * a.block_size) * tok_stride;
+#pragma unroll
+  for (int k = 0; k < NL; ++k) c.k[k] = load16(kbase + c.off + 4 * k * tok_stride);
+#pragma unroll
+  for (int k = 0; k < NL; ++k) c.v[k] = load16(vbase + c.off + 4 * k * tok_stride);
+}
+
 // Chunk of 4*NL tokens starting at logical position `base` (a multiple of
 // 4*NL that divides block_size, so the chunk lies in one cache block).  The
 // table index is clamped into the row, and an entry outside the cache reads
@@ -120,16 +137,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<NL>& c, const DecodeArgs& a
                                            int64_t blk_stride, int base) {
   const bool dummy = base < 0;
   const int lb = dummy ? 0 : min(base / a.block_size, a.max_blocks_per_seq - 1);
-  int blk = bt[lb];
-  c.ok = !dummy && static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
-  blk = c.ok ? blk : 0;
-  c.off = dummy ? 0
-                : static_cast<int64_t>(blk) * blk_stride +
-                      static_cast<int64_t>(base - lb * a.block_size) * tok_stride;
-#pragma unroll
-  for (int k = 0; k < NL; ++k) c.k[k] = load16(kbase + c.off + 4 * k * tok_stride);
-#pragma unroll
-  for (int k = 0; k < NL; ++k) c.v[k] = load16(vbase + c.off + 4 * k * tok_stride);
+  load_chunk_at<NL>(c, a, bt[lb], lb, dummy, kbase, vbase, tok_stride, blk_stride, base);
 }
 
 // Work order by length.  Workgroups are dealt round-robin over the 8 XCDs and
@@ -141,7 +149,8 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<NL>& c, const DecodeArgs& a
 // get the shortest next, which evens out the bytes each CU streams, and the
 // longest items start first.  Every wavefront ranks the <= 64 context lengths
 // itself (one per lane, ties by index), so no wavefront waits on another.
-__device__ __forceinline__ void length_ordered_item(const DecodeArgs& a, int by, int bz, int& b, int& g) {
+__device__ __forceinline__ void length_ordered_item(const DecodeArgs& a, int by, int bz, int& b, int& g,
+                                                    int& blk0) {
   const int lane = threadIdx.x & (kWave - 1);
   const int B = a.num_seqs;
   const int w = by + a.num_kv_heads * bz;
@@ -154,7 +163,9 @@ __device__ __forceinline__ void length_ordered_item(const DecodeArgs& a, int by,
   const int cap = min(a.max_blocks_per_seq * a.block_size, a.max_context_len);
   // Unique keys, larger = earlier: length, then lower index first; 0 = no sequence.
   uint32_t key = 0;
+  int e0 = 0;   // the sequence's first block-table entry, loaded with its length
   if (lane < B) {
+    e0 = a.block_tables[static_cast<int64_t>(lane) * a.max_blocks_per_seq];
     const int L = min(max(seq_len(a, lane), 0), cap);
     key = ((static_cast<uint32_t>(L) << 6) | static_cast<uint32_t>(63 - lane)) + 1u;
   }
@@ -173,6 +184,7 @@ __device__ __forceinline__ void length_ordered_item(const DecodeArgs& a, int by,
   }
   const uint64_t hit = cand;
   b = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit)));
+  blk0 = __builtin_amdgcn_readlane(e0, b);
 }
 
 // One workgroup's work; (bx, by, bz) = (partition, KV head, sequence) in the
@@ -218,8 +230,8 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int row = lane >> 4;   // which of the 4 tokens of a load
   const int col = lane & 15;   // which 16-byte column of the head row
-  int b = bz, g = by;
-  if (a.length_order) length_ordered_item(a, by, bz, b, g);
+  int b = bz, g = by, blk0 = 0;
+  if (a.length_order) length_ordered_item(a, by, bz, b, g, blk0);
   const int pi = bx;
   const int hq = a.num_kv_heads * G;
 
@@ -236,8 +248,15 @@ __device__ __forceinline__ void decode_partition_body(const DecodeArgs& a, int b
   // partition turns out to be empty.
   const bool spec = a.sliding_window == 0;
   ChunkRegs<NL> ca, cb;
-  if (spec) load_chunk<NL>(ca, a, bt, kbase, vbase, tok_stride, blk_stride,
-                           pi * a.partition_size + wave * CT);
+  if (spec) {
+    const int base0 = pi * a.partition_size + wave * CT;
+    // With the ranked order the table entry of block 0 came with the ranking
+    // (one round trip less before the first K/V loads).
+    if (a.length_order && base0 < a.block_size)
+      load_chunk_at<NL>(ca, a, blk0, 0, false, kbase, vbase, tok_stride, blk_stride, base0);
+    else
+      load_chunk<NL>(ca, a, bt, kbase, vbase, tok_stride, blk_stride, base0);
+  }
 
   const SeqRange r = seq_range(a, b);
   if (r.row < 0) return;
