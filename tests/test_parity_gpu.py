@@ -252,6 +252,40 @@ def test_decode_length_ordered_batches(gpu_lib, case):
             assert not out[b].any()
 
 
+@pytest.mark.parametrize("bs", [16, 32, 48, 64])
+def test_decode_length_ordered_small_blocks(gpu_lib, bs):
+    """Ranked decode (40 seqs, one partition each) at block sizes where some
+    wavefronts' first chunk lies past block 0: those read their table entry in
+    the loop, the others take the one the ranking loaded."""
+    lens = np.random.default_rng([46, bs]).integers(1, 700, size=40).tolist()
+    x = _random_case([47, bs], lens, bs=bs)
+    assert gpu_lib.decode_plan(len(lens), 8, max(lens))[1] == 1
+    out = run_decode(gpu_lib, to_torch(x, "cuda"), x)
+    assert_close(out, oracle_decode(x))
+
+
+def test_decode_length_ordered_bad_first_block(gpu_lib):
+    """Ranked decode with block 0 of some sequences outside the cache (the
+    entry the ranking preloads): those 64 keys contribute nothing."""
+    rng = np.random.default_rng(48)
+    lens = rng.integers(65, 700, size=40).tolist()
+    x = _random_case([49], lens, bs=64)
+    nb = x.k_cache.shape[0]
+    bad = {3: -5, 17: nb, 30: 1 << 30}
+    good_tables = x.block_tables.copy()
+    for b, e in bad.items():
+        x.block_tables[b, 0] = e
+    assert gpu_lib.decode_plan(len(lens), 8, max(lens))[1] == 1
+    out = run_decode(gpu_lib, to_torch(x, "cuda"), x)
+    ref = oracle_decode(W.PagedInputs(**{**x.__dict__, "block_tables": good_tables}))
+    for b in bad:
+        # keys 64 .. L-1 only: the sequence's blocks from the second on
+        tb = np.ascontiguousarray(good_tables[b:b + 1, 1:])
+        ref[b:b + 1] = oracle.paged_decode(x.q[b:b + 1], x.k_cache, x.v_cache, tb,
+                                           np.array([lens[b] - 64], np.int32), x.scale)
+    assert_close(out, ref)
+
+
 def test_decode_block_permutation_bit_exact(gpu_lib):
     x = _random_case([34], [37, 513, 900, 1024], bs=64)
     out1 = run_decode(gpu_lib, to_torch(x, "cuda"), x, partition_size=256)
