@@ -12,9 +12,13 @@ graph and replayed (the pages' decode runs with graph replay); the eager rate
 is reported next to it.
 
 Further legs, each timed alone: the varlen prefill over a cached prefix (16
-seqs, new U{64..512}, prefix 0-2 blocks; MFMA utilisation), the long-context
-decode (64 seqs, context U{4096..8192}, with and without a 256-token window;
-HBM fraction) and the two small decode workloads (latency).
+seqs, new U{64..512}, prefix 0-2 blocks; MFMA utilisation; also fused with the
+new tokens' store), the long-context decode (64 seqs, context U{4096..8192},
+with and without a 256-token window; HBM fraction), the two small decode
+workloads (latency), a mixed batch (48 decode rows + 4 prefill chunks, as one
+varlen prefill and split by kind in one launch) and the 28-layer step at
+context 512 for c = 1, 8 and 64, eager against graph replay (`--no-sweep`
+skips it; `--no-legs` skips every leg).
 
 Prints ONE JSON line.  `value` = algorithmic bytes of the step (K/V read by
 decode for the admitted positions, q, out, block tables, kv_store traffic) /
