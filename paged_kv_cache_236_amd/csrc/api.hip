@@ -517,8 +517,10 @@ pk_status prefill_common(void* out, const void* q, const void* k_new, const void
     // Items ranked by their key-tile count in each workgroup (longest first)
     // when there are few enough of them; else latest query tile first.
     const int64_t bm = 128 / a.group;
-    const int64_t items = static_cast<int64_t>(num_seqs) * ((max_seqlen_q + bm - 1) / bm);
+    const int64_t tiles = (max_seqlen_q + bm - 1) / bm;
+    const int64_t items = static_cast<int64_t>(num_seqs) * tiles;
     a.lpt_order = items <= pk::kPrefillRankMax ? 1 : 0;
+    a.tiles_recip = tiles > 1 ? static_cast<uint32_t>((int64_t{1} << 32) / tiles + 1) : 0u;
   }
   if (capture) {   // checked and built, launched by the caller
     *capture = a;

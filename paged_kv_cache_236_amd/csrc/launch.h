@@ -80,6 +80,9 @@ struct PrefillArgs {
   int32_t sliding_window;
   float scale_log2;
   int32_t lpt_order;       // 1: workgroups take (sequence, query tile) items by key-tile count, most first
+  uint32_t tiles_recip;    // lpt_order: floor(2^32 / query tiles per sequence) + 1 (0 for one tile),
+                           // so item k splits as k / tiles = mulhi(k, tiles_recip), exact while
+                           // k * tiles < 2^32 (items are < kPrefillRankMax here)
 };
 hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream);
 

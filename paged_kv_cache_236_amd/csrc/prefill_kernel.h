@@ -246,34 +246,39 @@ __device__ __forceinline__ u32x2_t read_tr16(const char* p) {
 // items last) and takes the item of rank bx / num_kv_heads, KV head
 // bx % num_kv_heads: longest processing time first.  Up to 128 items, two per
 // lane: a ballot radix select over the 6 count bits finds the count, then a
-// prefix count of the remaining candidates finds the item.  The lengths and first block-table entry of every
-// item's sequence are loaded in one round trip, and the chosen item's come
-// from the lane that loaded them.
+// prefix count of the remaining candidates finds the item; the candidate sets
+// are wave-wide masks, so the select runs on the scalar unit, and item k
+// splits into (sequence, tile) with a multiply by the host's reciprocal of the
+// tile count.  The lengths and first block-table entry of every item's
+// sequence are loaded in one round trip, and the chosen item's come from the
+// lane that loaded them.
 template <int BM>
 __device__ __forceinline__ void ranked_item(const PrefillArgs& a, int ntiles, int rank, int& b,
                                             int& t, int& q0, int& q1, int& k0, int& k1,
                                             int& blk0) {
-  constexpr int KPL = kPrefillRankMax / kWave;
+  static_assert(kPrefillRankMax == 2 * kWave, "two items per lane");
   const int lane = threadIdx.x & (kWave - 1);
-  b = t = q0 = q1 = k0 = k1 = blk0 = 0;   // (an item is always found: the keys are distinct)
   const int S = a.num_seqs * ntiles;
-  int vq0[KPL], vq1[KPL], vk0[KPL], vk1[KPL], vbt[KPL];
+  // Item k = lane + 64 j is query tile k % ntiles of sequence k / ntiles.
+  auto seq_of = [&](int k) __attribute__((always_inline)) {
+    return ntiles > 1 ? static_cast<int>(__umulhi(static_cast<uint32_t>(k), a.tiles_recip)) : k;
+  };
+  int vq0[2], vq1[2], vk0[2], vk1[2], vbt[2];
+  uint32_t cnt[2];
+  uint64_t cand[2];   // candidate items, one bit per lane
 #pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int k = min(lane + kWave * j, S - 1);
-    const int bb = k / ntiles;
+  for (int j = 0; j < 2; ++j) {
+    const int bb = seq_of(min(lane + kWave * j, S - 1));
     vq0[j] = a.cu_seqlens_q[bb];
     vq1[j] = a.cu_seqlens_q[bb + 1];
     vk0[j] = a.cu_seqlens_k[bb];
     vk1[j] = a.cu_seqlens_k[bb + 1];
     vbt[j] = a.block_tables[static_cast<int64_t>(bb) * a.max_blocks_per_seq];
   }
-  uint32_t cnt[KPL];
-  bool cand[KPL];
 #pragma unroll
-  for (int j = 0; j < KPL; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int k = lane + kWave * j;
-    const int tt = k % ntiles;
+    const int tt = k - seq_of(k) * ntiles;
     const int Lq = vq1[j] - vq0[j], Lk = vk1[j] - vk0[j], P = Lk - Lq, qa = tt * BM;
     int n = 0;
     if (!(Lq <= 0 || P < 0 || qa >= Lq || vq0[j] < 0 || vq0[j] + Lq > a.total_q)) {
@@ -281,47 +286,42 @@ __device__ __forceinline__ void ranked_item(const PrefillArgs& a, int ntiles, in
       const int kstart = a.sliding_window > 0 ? max(0, pos_lo - a.sliding_window + 1) : 0;
       n = pos_hi / kBN - kstart / kBN + 1;
     }
-    cand[j] = k < S;
     cnt[j] = static_cast<uint32_t>(min(n, 63));
+    cand[j] = __ballot(k < S);
   }
   // The count bucket holding rank `rank`, from the top bit down: among the
   // remaining candidates those with the bit set rank above those without.
+  // The candidate sets are wave-wide masks, so this runs on the scalar unit.
   int need = rank;
 #pragma unroll
   for (int bit = 5; bit >= 0; --bit) {
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) c += __builtin_popcountll(__ballot(cand[j] && ((cnt[j] >> bit) & 1u)));
+    const uint64_t ones0 = __ballot((cnt[0] >> bit) & 1u) & cand[0];
+    const uint64_t ones1 = __ballot((cnt[1] >> bit) & 1u) & cand[1];
+    const int c = __builtin_popcountll(ones0) + __builtin_popcountll(ones1);
     const bool in_ones = need < c;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      const bool set = (cnt[j] >> bit) & 1u;
-      cand[j] = cand[j] && (in_ones ? set : !set);
-    }
+    cand[0] = in_ones ? ones0 : cand[0] & ~ones0;
+    cand[1] = in_ones ? ones1 : cand[1] & ~ones1;
     need = in_ones ? need : need - c;
   }
   // Within the bucket, items in index order (k = lane + 64 j): the `need`-th
   // remaining candidate, found by each candidate's count of candidates below it.
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const uint64_t m = __ballot(cand[j]);
-    const int c = __builtin_popcountll(m);
-    if (need >= 0 && need < c) {
-      const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
-      const uint64_t w = __ballot(cand[j] && below == need);
-      const int src = __builtin_ctzll(w);
-      const int k = src + kWave * j;
-      b = k / ntiles;
-      t = k % ntiles;
-      q0 = __builtin_amdgcn_readlane(vq0[j], src);
-      q1 = __builtin_amdgcn_readlane(vq1[j], src);
-      k0 = __builtin_amdgcn_readlane(vk0[j], src);
-      k1 = __builtin_amdgcn_readlane(vk1[j], src);
-      blk0 = __builtin_amdgcn_readlane(vbt[j], src);
-    }
-    need -= c;
-  }
+  const int c0 = __builtin_popcountll(cand[0]);
+  const int j = need < c0 ? 0 : 1;
+  const uint64_t m = j == 0 ? cand[0] : cand[1];
+  need = j == 0 ? need : need - c0;
+  const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+  const bool mine = ((m >> lane) & 1u) && below == need;
+  const uint64_t hit = __ballot(mine);   // one lane: the rank is below the item count
+  const int src = hit ? static_cast<int>(__builtin_ctzll(hit)) : 0;
+  const int k = src + kWave * j;
+  b = seq_of(k);
+  t = k - b * ntiles;
+  q0 = __builtin_amdgcn_readlane(j == 0 ? vq0[0] : vq0[1], src);
+  q1 = __builtin_amdgcn_readlane(j == 0 ? vq1[0] : vq1[1], src);
+  k0 = __builtin_amdgcn_readlane(j == 0 ? vk0[0] : vk0[1], src);
+  k1 = __builtin_amdgcn_readlane(j == 0 ? vk1[0] : vk1[1], src);
+  blk0 = __builtin_amdgcn_readlane(j == 0 ? vbt[0] : vbt[1], src);
 }
 
 // POS: the softmax scale is positive, so the max of the raw scores gives the
@@ -349,8 +349,12 @@ __device__ __forceinline__ void paged_prefill_body(const PrefillArgs& a, int bx)
   const int ntiles = (a.max_seqlen_q + BM - 1) / BM;
   int t, b, g, q0, q1, k0, k1, blk_first;
   if (a.lpt_order) {
-    g = bx % a.num_kv_heads;
-    ranked_item<BM>(a, ntiles, bx / a.num_kv_heads, b, t, q0, q1, k0, k1, blk_first);
+    // rank bx / Hkv, KV head bx % Hkv (shifts for a power-of-two Hkv)
+    const int hkv = a.num_kv_heads;
+    const bool pow2 = (hkv & (hkv - 1)) == 0;
+    const int rank = pow2 ? bx >> __builtin_ctz(hkv) : bx / hkv;
+    g = pow2 ? bx & (hkv - 1) : bx - rank * hkv;
+    ranked_item<BM>(a, ntiles, rank, b, t, q0, q1, k0, k1, blk_first);
   } else {
     t = ntiles - 1 - bx / npairs;
     const int pr = bx % npairs;
